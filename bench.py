@@ -1,0 +1,319 @@
+"""Benchmark of the row-parallel GEMM + partial channel-reduce on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (one step): the Llama2-7B MLP down-projection as a row-parallel layer
+with partial channel-reduce, forward + backward: T = 8 ranks resident on the
+GPU, M = 4 x 4096 = 16384 tokens, K = 11008 (Kr = 1376 per rank), H = 4096,
+sync fraction p = 0.5 with a seeded random channel mask, bf16 inputs
+X ~ N(0,1), W ~ N(0,0.02), dZ ~ N(0,1), fp32 accumulation.  Inputs are
+synthetic and resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` is the step's algorithmic TFLOP/s
+(fwd 2MKH + bwd 4MKH flops).  Beside it: per-kernel times, the roofline of the
+dominant kernel, the standalone reduce in GB/s, the decode-shaped forward in
+GB/s, the attention out-projection (Kr = 512) and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused rowpar GEMM+partial-reduce TFLOP/s (% MFMA peak); reduce GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+T, M, KR, H, P = 8, 16384, 1376, 4096, 0.5
+KR_OUT = 512
+DEC_M = (1, 8, 32)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--only", default="", help="comma list of legs: train,out,reduce,decode (profiling runs)")
+    return ap.parse_args()
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "partial_channel_reduce_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(
+            "bench.py measures one GPU: the T tensor-parallel ranks are resident shards on a single "
+            "MI355X; runs on more than one GPU are not part of this build.",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from partial_channel_reduce_amd import ops, synth
+
+    ops.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    legs = set(args.only.split(",")) if args.only else {"train", "out", "reduce", "decode"}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def randn_bf16(shape, scale=1.0):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * scale).to(torch.bfloat16)
+
+    def mask_dev(Hh, seed=0):
+        return torch.from_numpy(synth.make_mask(Hh, P, "random", seed=seed)).to(dev)
+
+    def time_call(fn, iters, warm=2):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / iters  # ms
+
+    res = {}
+    K = T * KR
+    flops_fwd = 2.0 * M * K * H
+    flops_step = 3.0 * flops_fwd
+
+    # ------------------------------------------------------------------ train
+    if "train" in legs:
+        log("allocating 7B down-proj inputs")
+        X = randn_bf16((T, M, KR))
+        W = randn_bf16((T, KR, H), 0.02)
+        dZ = randn_bf16((T, M, H))
+        mk = mask_dev(H)
+        out = torch.empty((T, M, H), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty_like(X)
+        dW = torch.empty_like(W)
+        ws = torch.empty(ops.bwd_workspace_bytes(T, M, KR, H), dtype=torch.uint8, device=dev)
+
+        def step():
+            ops.rowpar_pcr_fwd(X, W, mk, out=out)
+            ops.pcr_bwd(dZ, X, W, mk, dX=dX, dW=dW, workspace=ws)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        log(f"timing {args.steps} steps")
+        t0 = time.perf_counter()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            step()
+        e.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_step = s.elapsed_time(e) / args.steps
+        res["ms_per_step"] = ms_step
+        res["wall_s"] = wall
+        log(f"step {ms_step:.3f} ms")
+
+        it = max(3, args.steps // 2)
+        t_fwd = time_call(lambda: ops.rowpar_pcr_fwd(X, W, mk, out=out), it)
+        t_bwd = time_call(lambda: ops.pcr_bwd(dZ, X, W, mk, dX=dX, dW=dW, workspace=ws), it)
+        t_bdx = time_call(lambda: ops.pcr_bwd(dZ, X, W, mk, dX=dX, need_dw=False, workspace=ws), it)
+        t_bdw = time_call(lambda: ops.pcr_bwd(dZ, X, W, mk, dW=dW, need_dx=False, workspace=ws), it)
+        k = {
+            "rowpar_pcr_fwd_kernel": t_fwd,
+            "pcr_bwd_dw_kernel": t_bwd - t_bdx,
+            "pcr_bwd_dx_kernel": t_bwd - t_bdw,
+            "grad_sync_sum_kernel": max(t_bdx + t_bdw - t_bwd, 0.0),
+        }
+        res["kernels_ms"] = {n: round(v, 4) for n, v in k.items()}
+        per_flops = {"rowpar_pcr_fwd_kernel": flops_fwd, "pcr_bwd_dw_kernel": flops_fwd, "pcr_bwd_dx_kernel": flops_fwd}
+        dom = max(per_flops, key=lambda n: k[n])
+        ach = per_flops[dom] / (k[dom] * 1e-3) / 1e12
+        res["dominant"] = dom
+        res["roofline"] = {
+            "bound": "mfma",
+            "kernel": dom,
+            "achieved": round(ach, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        }
+        res["fwd_tflops"] = round(flops_fwd / (t_fwd * 1e-3) / 1e12, 2)
+        res["bwd_tflops"] = round(2 * flops_fwd / (t_bwd * 1e-3) / 1e12, 2)
+        del X, W, dZ, out, dX, dW, ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------- out-projection
+    if "out" in legs:
+        Ko = T * KR_OUT
+        Xo = randn_bf16((T, M, KR_OUT))
+        Wo = randn_bf16((T, KR_OUT, H), 0.02)
+        dZo = randn_bf16((T, M, H))
+        mk = mask_dev(H)
+        outo = torch.empty((T, M, H), dtype=torch.bfloat16, device=dev)
+        dXo, dWo = torch.empty_like(Xo), torch.empty_like(Wo)
+        wso = torch.empty(ops.bwd_workspace_bytes(T, M, KR_OUT, H), dtype=torch.uint8, device=dev)
+        tf = time_call(lambda: ops.rowpar_pcr_fwd(Xo, Wo, mk, out=outo), 10)
+        tb = time_call(lambda: ops.pcr_bwd(dZo, Xo, Wo, mk, dX=dXo, dW=dWo, workspace=wso), 10)
+        fo = 2.0 * M * Ko * H
+        res["out_proj"] = {
+            "Kr": KR_OUT,
+            "fwd_ms": round(tf, 4),
+            "bwd_ms": round(tb, 4),
+            "fwd_bwd_tflops": round(3 * fo / ((tf + tb) * 1e-3) / 1e12, 2),
+        }
+        del Xo, Wo, dZo, outo, dXo, dWo, wso
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------ reduce-only fp32
+    if "reduce" in legs:
+        red = {}
+        mk = mask_dev(H, seed=1)
+        for Mr in (16384, 4096):
+            Y = torch.randn((T, Mr, H), generator=gen, device=dev, dtype=torch.float32)
+            o = torch.empty_like(Y)
+            t = time_call(lambda: ops.partial_channel_reduce(Y, mk, out=o), 10)
+            nbytes = 2.0 * T * Mr * H * 4
+            gbs = nbytes / (t * 1e-3) / 1e9
+            red[f"M{Mr}"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+            del Y, o
+        # decode-sized reduces: latency-bound, rotate 64 buffer sets (> the 256 MB last-level cache)
+        for Mr in DEC_M:
+            sets = [torch.randn((T, Mr, H), generator=gen, device=dev) for _ in range(64)]
+            outs = [torch.empty_like(x) for x in sets]
+            idx = [0]
+
+            def call():
+                i = idx[0] % len(sets)
+                idx[0] += 1
+                ops.partial_channel_reduce(sets[i], mk, out=outs[i])
+
+            t = time_call(call, 128)
+            nbytes = 2.0 * T * Mr * H * 4
+            red[f"M{Mr}"] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bound": "latency"}
+            del sets, outs
+        res["reduce_only_f32"] = red
+        torch.cuda.empty_cache()
+
+    # -------------------------------------------------- decode-shaped forward
+    if "decode" in legs:
+        dec = {}
+        mk = mask_dev(H)
+        nsets = 6  # 6 x 90 MB of weights: beyond the 256 MB last-level cache
+        Ws = [randn_bf16((T, KR, H), 0.02) for _ in range(nsets)]
+        for Md in DEC_M:
+            Xs = [randn_bf16((T, Md, KR)) for _ in range(nsets)]
+            outs = [torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+            idx = [0]
+
+            def call():
+                i = idx[0] % nsets
+                idx[0] += 1
+                ops.rowpar_pcr_fwd(Xs[i], Ws[i], mk, out=outs[i])
+
+            t = time_call(call, 60, warm=6)
+            nbytes = 2.0 * (T * Md * KR + T * KR * H + T * Md * H)
+            gbs = nbytes / (t * 1e-3) / 1e9
+            dec[f"M{Md}"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        res["decode_down_proj"] = dec
+        del Ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------- CPU oracle leg
+    cpu = None
+    if not args.no_cpu_baseline and "train" in legs:
+        cpu = cpu_baseline(args.cpu_sample_tokens)
+
+    value = None
+    if "ms_per_step" in res:
+        value = flops_step / (res["ms_per_step"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2) if value is not None else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res.get("ms_per_step", float("nan")), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama2-7B MLP down-projection, row-parallel + partial channel-reduce, fwd+bwd",
+            "T": T, "M": M, "K": K, "Kr": KR, "H": H, "p": P, "mask": "random",
+        },
+        "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4) if value is not None else None,
+        "roofline": res.get("roofline"),
+        "cpu_baseline": cpu,
+        "kernels_ms": res.get("kernels_ms"),
+        "fwd_tflops": res.get("fwd_tflops"),
+        "bwd_tflops": res.get("bwd_tflops"),
+        "out_proj": res.get("out_proj"),
+        "reduce_only_f32": res.get("reduce_only_f32"),
+        "decode_down_proj": res.get("decode_down_proj"),
+        "src": src_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(tokens: int):
+    """The CPU oracle (fp64 numpy) on a bounded sample of the same workload:
+    forward + backward of the down-projection for `tokens` of the 16384 tokens."""
+    import numpy as np
+
+    import oracle
+    from partial_channel_reduce_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    log(f"cpu oracle on {tokens} tokens, {threads} BLAS threads")
+    X, W = synth.make_fwd_inputs(T, tokens, KR, H, seed=0)
+    dZ = synth.make_grad(T, tokens, H, seed=0)
+    mask = synth.make_mask(H, P, "random", seed=0)
+    t0 = time.perf_counter()
+    oracle.rowpar_pcr_fwd(X, W, mask)
+    oracle.pcr_bwd(dZ, X, W, mask)
+    dt = time.perf_counter() - t0
+    flops = 6.0 * tokens * (T * KR) * H
+    return {
+        "value": round(flops / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fwd+bwd of {tokens} of {M} tokens (T={T}, Kr={KR}, H={H}, p={P}), fp64 numpy, {dt:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

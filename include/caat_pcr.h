@@ -1,0 +1,119 @@
+/*
+ * caat_pcr.h -- C ABI of the MI355X (gfx950) partial channel-reduce library.
+ *
+ * Method: "Tensor-Parallelism with Partially Synchronized Activations"
+ * (CAAT-Net; Lamprecht, Karnieli, Hanani, Giladi, Soudry, NeurIPS 2025,
+ * arXiv 2506.19645), Introduction.  In tensor parallelism each of T ranks
+ * computes a partial activation with its row-parallel linear layer
+ * (attention out-projection, MLP down-projection); the usual all-reduce sums
+ * those partials.  The partial channel-reduce sums only the hidden channels
+ * of a sync set S and leaves every other channel with the rank's own value,
+ * so ranks hold different activations afterwards.  No channel synced is an
+ * ensemble of independent ranks; all channels synced is the ordinary layer.
+ *
+ * The T ranks are T shards resident in one GPU's memory:
+ *   X   [T, M, Kr]  bf16   rank t's input slice (Kr = K / T features)
+ *   W   [T, Kr, H]  bf16   rank t's weight slice
+ *   mask[H]         uint8  nonzero = channel c is in S (the mask is S; the
+ *                          fraction p of the paper is |S| / H)
+ *   out [T, M, H]   bf16   rank t's activation after the partial reduce
+ * All arrays are dense row-major (last index contiguous).  bf16 values are
+ * passed as their raw 16-bit patterns.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller; the library keeps no
+ *     reference after the call returns and allocates nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream) and runs asynchronously; nothing synchronises or prints.
+ *   - Arguments are validated on the host before any GPU work is enqueued; on
+ *     an error nothing is enqueued and the status code says why.
+ *   - Sizes: 1 <= T <= 64; M >= 0 (M == 0 enqueues nothing, and tensors
+ *     with no elements may then be NULL); Kr and H are positive multiples of
+ *     8; one rank's slices (M*Kr, Kr*H, M*H elements) stay below 2^31.
+ *     Tensor pointers must be 16-byte aligned, the mask 8-byte aligned.
+ *   - Sums of synced channels are taken in fp32, in ascending rank order,
+ *     once per element, and the one result is written to every rank, so the
+ *     synced channels are bit-identical across ranks and run to run.
+ *   - Calls that share a workspace must not run concurrently.
+ */
+#ifndef CAAT_PCR_H
+#define CAAT_PCR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CAAT_OK = 0,
+  CAAT_ERR_NULL = 1,      /* a required pointer is NULL */
+  CAAT_ERR_DIM = 2,       /* a size is out of range or not a multiple of 8 */
+  CAAT_ERR_ALIGN = 3,     /* a pointer is misaligned */
+  CAAT_ERR_ALIAS = 4,     /* an output overlaps an input (or another output) */
+  CAAT_ERR_DTYPE = 5,     /* unknown dtype code */
+  CAAT_ERR_WORKSPACE = 6, /* workspace missing or smaller than required */
+  CAAT_ERR_LAUNCH = 7     /* the HIP runtime rejected a kernel launch */
+} caat_status;
+
+typedef enum { CAAT_F32 = 0, CAAT_BF16 = 1 } caat_dtype;
+
+/* Version of this ABI (incremented on incompatible change). */
+int caat_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* caat_status_string(int status);
+
+/*
+ * Forward: row-parallel linear layer followed by the partial channel-reduce
+ * (Introduction of the paper):
+ *   Y_t = X_t W_t                      (bf16 products, fp32 accumulation)
+ *   out[t][:, c] = sum_u Y_u[:, c]     for c in S   (same value on every rank)
+ *   out[t][:, c] = Y_t[:, c]           for c not in S
+ * rounded once to bf16 (nearest even).  `out` must not overlap X, W or mask.
+ * M <= 32 (decode-shaped calls) uses a weight-streaming kernel that needs
+ * caat_rowpar_pcr_fwd_workspace_bytes() bytes of workspace, zero-filled before
+ * its first use (caat_workspace_init); each call leaves it zero-filled again.
+ * Other M need no workspace (pass NULL, 0).
+ */
+int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out,
+                        int T, int M, int Kr, int H,
+                        void* workspace, size_t workspace_bytes, void* stream);
+size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
+
+/*
+ * Backward of caat_rowpar_pcr_fwd for per-rank incoming gradients dZ[T,M,H]
+ * (bf16).  The partial channel-reduce is linear and self-adjoint, which is
+ * the forward/backward agreement the paper's Introduction requires:
+ *   G_t[:, c] = sum_u dZ_u[:, c]  for c in S,   dZ_t[:, c]  for c not in S
+ *   dX[t] = G_t W_t^T   [M, Kr] bf16      dW[t] = X_t^T G_t   [Kr, H] bf16
+ * G's synced channels are rounded to bf16 once (they feed bf16 MFMA); both
+ * products accumulate in fp32.  dX or dW may be NULL to skip that product.
+ * Needs caat_pcr_bwd_workspace_bytes() bytes of workspace (any contents).
+ * Outputs must not overlap the inputs or each other.
+ */
+int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask,
+                 uint16_t* dX, uint16_t* dW, int T, int M, int Kr, int H,
+                 void* workspace, size_t workspace_bytes, void* stream);
+size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H);
+
+/*
+ * The partial channel-reduce alone, on given per-rank activations Y[T,M,H]
+ * of `dtype` (CAAT_F32 or CAAT_BF16):
+ *   out[t][:, c] = Y[0][:, c] + Y[1][:, c] + ... + Y[T-1][:, c]   for c in S
+ *   out[t][:, c] = Y[t][:, c]                                      for c not in S
+ * (fp32 sum in that order; bf16 rounds the sum once).  out == Y runs in
+ * place and never writes the local channels; otherwise out must not overlap Y.
+ */
+int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out,
+                                int T, int M, int H, int dtype, void* stream);
+
+/* Zero-fill `bytes` of workspace on `stream` (bytes a multiple of 4). */
+int caat_workspace_init(void* workspace, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAAT_PCR_H */

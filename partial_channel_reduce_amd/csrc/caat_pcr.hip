@@ -1,0 +1,229 @@
+// C ABI of the partial channel-reduce library: host-side validation and kernel
+// dispatch.  Declarations and the contract of every call are in caat_pcr.h.
+#include "caat_pcr.h"
+
+#include <hip/hip_runtime.h>
+
+#include "decode_kernel.hpp"
+#include "gemm_kernels.hpp"
+#include "reduce_kernels.hpp"
+
+namespace {
+
+using namespace caat;
+
+constexpr int kMaxT = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_dims(int T, int M, int Kr, int H) {
+  if (T < 1 || T > kMaxT || M < 0 || Kr < 8 || H < 8) return CAAT_ERR_DIM;
+  if (Kr % 8 != 0 || H % 8 != 0) return CAAT_ERR_DIM;
+  // element counts of the largest tensor must fit the kernels' 64-bit offsets
+  // and the grid sizes (<= 2^31 workgroups)
+  if ((long long)T * M * (long long)(H > Kr ? H : Kr) > (1LL << 40)) return CAAT_ERR_DIM;
+  // one rank's slices are addressed with 32-bit element offsets
+  const long long lim = 1LL << 31;
+  if ((long long)M * Kr >= lim || (long long)Kr * H >= lim || (long long)M * H >= lim) return CAAT_ERR_DIM;
+  return CAAT_OK;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? CAAT_OK : CAAT_ERR_LAUNCH; }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+template <int BM, int BN>
+int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
+               int H, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (H + BN - 1) / BN;
+  hipLaunchKernelGGL((rowpar_pcr_fwd_kernel<BM, BN>), dim3(tm * tn), dim3(kGemmThreads), 0, s, X, W, mask, out, T,
+                     M, Kr, H, tm, tn);
+  return launched();
+}
+
+template <int BM, int BN>
+int launch_dx(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* W, const uint8_t* mask, uint16_t* dX, int T,
+              int M, int Kr, int H, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (Kr + BN - 1) / BN;
+  hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, dZ, Gs, W, mask, dX,
+                     T, M, Kr, H, tm, tn);
+  return launched();
+}
+
+template <int BM, int BN>
+int launch_dw(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* X, const uint8_t* mask, uint16_t* dW, int T,
+              int M, int Kr, int H, hipStream_t s) {
+  const int tm = (Kr + BM - 1) / BM, tn = (H + BN - 1) / BN;
+  hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, dZ, Gs, X, mask, dW,
+                     T, M, Kr, H, tm, tn);
+  return launched();
+}
+
+// Large tiles when they still give every CU work, else 128 x 128.
+bool use_big_tiles(long long rows, long long cols, long long batch) {
+  return ((rows + 255) / 256) * ((cols + 255) / 256) * batch >= 512;
+}
+
+}  // namespace
+
+extern "C" {
+
+int caat_abi_version(void) { return 1; }
+
+const char* caat_status_string(int status) {
+  switch (status) {
+    case CAAT_OK: return "ok";
+    case CAAT_ERR_NULL: return "null pointer";
+    case CAAT_ERR_DIM: return "invalid dimensions (need 1<=T<=64, M>=0, Kr and H positive multiples of 8)";
+    case CAAT_ERR_ALIGN: return "misaligned pointer (tensors 16-byte, mask 8-byte)";
+    case CAAT_ERR_ALIAS: return "output overlaps an input or another output";
+    case CAAT_ERR_DTYPE: return "unknown dtype";
+    case CAAT_ERR_WORKSPACE: return "workspace missing or too small";
+    case CAAT_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
+  if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0 || M > kDecMaxM) return 0;
+  return dec_counter_bytes(H) + round256((size_t)T * M * H * sizeof(float));
+}
+
+int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M,
+                        int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = check_dims(T, M, Kr, H)) return st;
+  // tensors with no elements (M == 0) may be passed as NULL
+  if (!W || !mask || (M > 0 && (!X || !out))) return CAAT_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(out, 16) || !aligned(mask, 8)) return CAAT_ERR_ALIGN;
+  const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nO = (size_t)T * M * H * 2;
+  if (overlap(out, nO, X, nX) || overlap(out, nO, W, nW) || overlap(out, nO, mask, H)) return CAAT_ERR_ALIAS;
+  const size_t need = caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return CAAT_ERR_WORKSPACE;
+    if (overlap(workspace, need, out, nO) || overlap(workspace, need, X, nX) || overlap(workspace, need, W, nW))
+      return CAAT_ERR_ALIAS;
+  }
+  if (M == 0) return CAAT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (M <= kDecMaxM) {
+    uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
+    float* partial = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + dec_counter_bytes(H));
+    const int nblocks = (H + kDecBN - 1) / kDecBN;
+    hipLaunchKernelGGL(rowpar_pcr_decode_kernel, dim3(nblocks * T), dim3(kGemmThreads), 0, s, X, W, mask, out,
+                       counters, partial, T, M, Kr, H);
+    return launched();
+  }
+  return launch_fwd<128, 128>(X, W, mask, out, T, M, Kr, H, s);
+}
+
+size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H) {
+  if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0) return 0;
+  return round256((size_t)M * H * 2);
+}
+
+int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* dX,
+                 uint16_t* dW, int T, int M, int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = check_dims(T, M, Kr, H)) return st;
+  // dZ and X have no elements when M == 0 and may then be NULL
+  if (!mask || (M > 0 && !dZ) || (dX && !W) || (M > 0 && dW && !X)) return CAAT_ERR_NULL;
+  if (!aligned(dZ, 16) || (X && !aligned(X, 16)) || (W && !aligned(W, 16)) || (dX && !aligned(dX, 16)) ||
+      (dW && !aligned(dW, 16)) || !aligned(mask, 8))
+    return CAAT_ERR_ALIGN;
+  const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nZ = (size_t)T * M * H * 2;
+  const void* ins[4] = {dZ, X, W, mask};
+  const size_t nin[4] = {nZ, nX, nW, (size_t)H};
+  for (int i = 0; i < 4; ++i) {
+    if (!ins[i]) continue;
+    if (dX && overlap(dX, nX, ins[i], nin[i])) return CAAT_ERR_ALIAS;
+    if (dW && overlap(dW, nW, ins[i], nin[i])) return CAAT_ERR_ALIAS;
+  }
+  if (dX && dW && overlap(dX, nX, dW, nW)) return CAAT_ERR_ALIAS;
+  const size_t need = caat_pcr_bwd_workspace_bytes(T, M, Kr, H);
+  if (need > 0 && (dX || dW)) {
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return CAAT_ERR_WORKSPACE;
+    for (int i = 0; i < 4; ++i)
+      if (ins[i] && overlap(workspace, need, ins[i], nin[i])) return CAAT_ERR_ALIAS;
+    if ((dX && overlap(workspace, need, dX, nX)) || (dW && overlap(workspace, need, dW, nW))) return CAAT_ERR_ALIAS;
+  }
+  if (!dX && !dW) return CAAT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (M == 0) {  // no tokens: dX is empty and dW = X^T G is the zero matrix
+    if (dW) {
+      const long long n = (long long)T * Kr * H / 2;  // u32 words of bf16 zeros
+      hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                         reinterpret_cast<uint32_t*>(dW), n, 0u);
+      return launched();
+    }
+    return CAAT_OK;
+  }
+  uint16_t* Gs = reinterpret_cast<uint16_t*>(workspace);
+  const long long nvec = (long long)M * (H / 8);
+  hipLaunchKernelGGL(grad_sync_sum_kernel, dim3((unsigned)((nvec + kReduceThreads - 1) / kReduceThreads)),
+                     dim3(kReduceThreads), 0, s, dZ, mask, Gs, T, nvec, H / 8, (long long)M * H);
+  if (int st = launched()) return st;
+  if (dX) {
+    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256>(dZ, Gs, W, mask, dX, T, M, Kr, H, s)
+                                           : launch_dx<128, 128>(dZ, Gs, W, mask, dX, T, M, Kr, H, s);
+    if (st) return st;
+  }
+  if (dW) {
+    const int st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256>(dZ, Gs, X, mask, dW, T, M, Kr, H, s)
+                                           : launch_dw<128, 128>(dZ, Gs, X, mask, dW, T, M, Kr, H, s);
+    if (st) return st;
+  }
+  return CAAT_OK;
+}
+
+int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, int T, int M, int H, int dtype,
+                                void* stream) {
+  if (dtype != CAAT_F32 && dtype != CAAT_BF16) return CAAT_ERR_DTYPE;
+  if (T < 1 || T > kMaxT || M < 0 || H < 8 || H % 8 != 0) return CAAT_ERR_DIM;
+  if (!mask || (M > 0 && (!Y || !out))) return CAAT_ERR_NULL;
+  if ((long long)T * M * (long long)H > (1LL << 40)) return CAAT_ERR_DIM;
+  if (!aligned(Y, 16) || !aligned(out, 16) || !aligned(mask, 8)) return CAAT_ERR_ALIGN;
+  const size_t esz = dtype == CAAT_F32 ? 4 : 2;
+  const size_t n = (size_t)T * M * H * esz;
+  const bool inplace = (Y == out);
+  if (!inplace && overlap(Y, n, out, n)) return CAAT_ERR_ALIAS;
+  if (overlap(out, n, mask, H)) return CAAT_ERR_ALIAS;
+  if (M == 0) return CAAT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const long long mh = (long long)M * H;
+  if (dtype == CAAT_F32) {
+    const long long nvec = mh / 4;
+    const dim3 grid((unsigned)((nvec + kReduceThreads - 1) / kReduceThreads));
+    const float* y = static_cast<const float*>(Y);
+    float* o = static_cast<float*>(out);
+    const int ip = inplace ? 1 : 0;
+    switch (T) {
+      case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
+      case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
+      case 4: hipLaunchKernelGGL(pcr_reduce_f32_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
+      case 8: hipLaunchKernelGGL(pcr_reduce_f32_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
+      default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
+    }
+  } else {
+    const long long nvec = mh / 8;
+    const dim3 grid((unsigned)((nvec + kReduceThreads - 1) / kReduceThreads));
+    hipLaunchKernelGGL(pcr_reduce_bf16_kernel, grid, dim3(kReduceThreads), 0, s, static_cast<const uint16_t*>(Y),
+                       mask, static_cast<uint16_t*>(out), T, nvec, H / 8, mh, inplace ? 1 : 0);
+  }
+  return launched();
+}
+
+int caat_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return CAAT_OK;
+  if (!workspace) return CAAT_ERR_NULL;
+  if (!aligned(workspace, 4) || bytes % 4 != 0) return CAAT_ERR_ALIGN;
+  const long long n = (long long)(bytes / 4);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace), n, 0u);
+  return launched();
+}
+
+}  // extern "C"

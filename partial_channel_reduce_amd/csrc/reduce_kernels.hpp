@@ -1,0 +1,195 @@
+// HBM-streaming kernels of the partial channel-reduce:
+//   * the standalone reduce over per-rank activations Y[T,M,H] (fp32 or bf16);
+//   * the backward's sync-set gradient Gs[m,c] = sum_t dZ[t,m,c] for c in S.
+//
+// Definition (CAAT-Net paper, Introduction): only the hidden channels of the
+// sync set S are summed over the T tensor-parallel ranks; the other channels
+// keep each rank's own value.  Sums run in fp32 in ascending rank order,
+// starting from rank 0's value, are formed once per (m, c) and written to every
+// rank, so the synced channels are bit-identical across ranks.
+#pragma once
+
+#include "common.hpp"
+
+namespace caat {
+
+constexpr int kReduceThreads = 256;
+
+// ---- fp32: one thread per 4-channel, 16-byte vector ---------------------------
+
+template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
+__global__ void __launch_bounds__(kReduceThreads)
+pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* out,
+                      int T_rt, long long nvec, int hvec, long long mh, int inplace) {
+  const int T = TC > 0 ? TC : T_rt;
+  const long long v = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+  if (v >= nvec) return;
+  const int c = (int)(v % hvec) * 4;
+  const long long m = v / hvec;
+  const long long base = m * (long long)hvec * 4 + c;  // element offset inside one rank
+  const uint32_t mk = *reinterpret_cast<const uint32_t*>(mask + c);
+  const bool s0 = (mk & 0xffu) != 0, s1 = (mk & 0xff00u) != 0;
+  const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
+  const bool any = s0 | s1 | s2 | s3;
+  const bool all = s0 & s1 & s2 & s3;
+
+  if (!any) {  // only local channels: copy through (nothing to do in place)
+    if (!inplace) {
+      for (int t = 0; t < T; ++t) {
+        const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + t * mh + base));
+        __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(out + t * mh + base));
+      }
+    }
+    return;
+  }
+
+  if (TC > 0) {
+    // All T vectors stay in registers: T loads in flight, then T stores.
+    f32x4 y[TC > 0 ? TC : 1];
+#pragma unroll
+    for (int t = 0; t < (TC > 0 ? TC : 1); ++t)
+      y[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + t * mh + base));
+    f32x4 s = y[0];
+#pragma unroll
+    for (int t = 1; t < (TC > 0 ? TC : 1); ++t) s += y[t];
+#pragma unroll
+    for (int t = 0; t < (TC > 0 ? TC : 1); ++t) {
+      float* o = out + t * mh + base;
+      if (all || !inplace) {
+        f32x4 w;
+        w.x = s0 ? s.x : y[t].x;
+        w.y = s1 ? s.y : y[t].y;
+        w.z = s2 ? s.z : y[t].z;
+        w.w = s3 ? s.w : y[t].w;
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(o));
+      } else {  // in place, mixed vector: touch only the synced channels
+        if (s0) o[0] = s.x;
+        if (s1) o[1] = s.y;
+        if (s2) o[2] = s.z;
+        if (s3) o[3] = s.w;
+      }
+    }
+  } else {
+    // Runtime T: first pass sums, second pass writes (re-reading rank t's
+    // vector for the local channels of a mixed vector).
+    f32x4 s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + base));
+    for (int t = 1; t < T; ++t) s += *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+    for (int t = 0; t < T; ++t) {
+      float* o = out + t * mh + base;
+      if (all) {
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(o));
+      } else if (!inplace) {
+        const f32x4 y = *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+        f32x4 w;
+        w.x = s0 ? s.x : y.x;
+        w.y = s1 ? s.y : y.y;
+        w.z = s2 ? s.z : y.z;
+        w.w = s3 ? s.w : y.w;
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(o));
+      } else {
+        if (s0) o[0] = s.x;
+        if (s1) o[1] = s.y;
+        if (s2) o[2] = s.z;
+        if (s3) o[3] = s.w;
+      }
+    }
+  }
+}
+
+// ---- bf16: one thread per 8-channel, 16-byte vector ---------------------------
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float f[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f[2 * d] = bf16_lo(v[d]);
+    f[2 * d + 1] = bf16_hi(v[d]);
+  }
+}
+
+// 0xffff per synced bf16 lane of an 8-channel vector, from 8 mask bytes.
+__device__ __forceinline__ u32x4 expand_mask8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = ((lo & 0xffu) ? 0xffffu : 0u) | ((lo & 0xff00u) ? 0xffff0000u : 0u);
+  r[1] = ((lo & 0xff0000u) ? 0xffffu : 0u) | ((lo & 0xff000000u) ? 0xffff0000u : 0u);
+  r[2] = ((hi & 0xffu) ? 0xffffu : 0u) | ((hi & 0xff00u) ? 0xffff0000u : 0u);
+  r[3] = ((hi & 0xff0000u) ? 0xffffu : 0u) | ((hi & 0xff000000u) ? 0xffff0000u : 0u);
+  return r;
+}
+
+__global__ void __launch_bounds__(kReduceThreads)
+pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint16_t* out,
+                       int T, long long nvec, int hvec, long long mh, int inplace) {
+  const long long v = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+  if (v >= nvec) return;
+  const int c = (int)(v % hvec) * 8;
+  const long long m = v / hvec;
+  const long long base = m * (long long)hvec * 8 + c;
+  const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
+  if ((mk[0] | mk[1]) == 0u) {
+    if (!inplace)
+      for (int t = 0; t < T; ++t) st16_nt(out + t * mh + base, ld16(Y + t * mh + base));
+    return;
+  }
+  const u32x4 sel = expand_mask8(mk[0], mk[1]);
+  float s[8];
+  bf16x8_to_f32(ld16(Y + base), s);
+  for (int t = 1; t < T; ++t) {
+    float f[8];
+    bf16x8_to_f32(ld16(Y + t * mh + base), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += f[e];
+  }
+  u32x4 sv;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
+  const bool all = (sel[0] & sel[1] & sel[2] & sel[3]) == 0xffffffffu;
+  for (int t = 0; t < T; ++t) {
+    uint16_t* o = out + t * mh + base;
+    if (all) {
+      st16_nt(o, sv);
+    } else if (!inplace) {
+      const u32x4 y = ld16(Y + t * mh + base);
+      st16_nt(o, (sv & sel) | (y & ~sel));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((sel[e >> 1] >> (16 * (e & 1))) & 1u) o[e] = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// ---- backward: Gs[m, c] = bf16( sum_t dZ[t, m, c] ) for c in S ---------------
+// Gs is [M, H] bf16; vectors with no synced channel are skipped (never read by
+// the GEMM loaders, which select Gs only where the mask is set).
+__global__ void __launch_bounds__(kReduceThreads)
+grad_sync_sum_kernel(const uint16_t* __restrict__ dZ, const uint8_t* __restrict__ mask,
+                     uint16_t* __restrict__ Gs, int T, long long nvec, int hvec, long long mh) {
+  const long long v = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+  if (v >= nvec) return;
+  const int c = (int)(v % hvec) * 8;
+  const long long m = v / hvec;
+  const long long base = m * (long long)hvec * 8 + c;
+  const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
+  if ((mk[0] | mk[1]) == 0u) return;
+  float s[8];
+  bf16x8_to_f32(ld16(dZ + base), s);
+  for (int t = 1; t < T; ++t) {
+    float f[8];
+    bf16x8_to_f32(ld16(dZ + t * mh + base), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += f[e];
+  }
+  u32x4 sv;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
+  st16(Gs + base, sv);
+}
+
+// Small fill kernel (used instead of a runtime memset so the call sequence can
+// be captured in a graph).
+__global__ void fill_u32_kernel(uint32_t* p, long long n, uint32_t v) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace caat

@@ -1,0 +1,211 @@
+"""Python binding of libcaat_pcr.so (C ABI in include/caat_pcr.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the
+library is not built, every call raises; there is no fallback path.
+
+Tensors: bf16 tensors are torch.bfloat16, the mask is torch.uint8 [H]
+(nonzero = channel in the sync set S), all on the same GPU and contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import LIBPATH
+
+CAAT_OK = 0
+CAAT_F32 = 0
+CAAT_BF16 = 1
+STATUS_NAMES = {
+    0: "CAAT_OK",
+    1: "CAAT_ERR_NULL",
+    2: "CAAT_ERR_DIM",
+    3: "CAAT_ERR_ALIGN",
+    4: "CAAT_ERR_ALIAS",
+    5: "CAAT_ERR_DTYPE",
+    6: "CAAT_ERR_WORKSPACE",
+    7: "CAAT_ERR_LAUNCH",
+}
+
+# (name, restype, argtypes) for every symbol the header declares.
+_P, _I, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = [
+    ("caat_abi_version", _I, []),
+    ("caat_status_string", ctypes.c_char_p, [_I]),
+    ("caat_rowpar_pcr_fwd", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
+    ("caat_rowpar_pcr_fwd_workspace_bytes", _S, [_I, _I, _I, _I]),
+    ("caat_pcr_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
+    ("caat_pcr_bwd_workspace_bytes", _S, [_I, _I, _I, _I]),
+    ("caat_partial_channel_reduce", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    ("caat_workspace_init", _I, [_P, _S, _P]),
+]
+
+
+class CaatError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().caat_status_string(status).decode() if _LIB is not None else ""
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
+
+
+_LIB = None
+_LOCK = threading.Lock()
+
+
+def lib(path: str | None = None) -> ctypes.CDLL:
+    """Load the built library (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    with _LOCK:
+        p = path or LIBPATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is not built; run `python -m partial_channel_reduce_amd.build` "
+                "(the HIP library is required; there is no CPU path)"
+            )
+        L = ctypes.CDLL(p)
+        for name, res, args in SIGNATURES:
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _LIB = L
+        return L
+
+
+def _check(status: int, where: str):
+    if status != CAAT_OK:
+        raise CaatError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# Zero-filled workspaces for the decode-shaped forward, per device.  Each call
+# leaves its counters zeroed, so sequential calls on one stream may share one.
+_WS: dict = {}
+
+
+def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    key = (dev.type, dev.index)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        _WS[key] = ws
+    return ws
+
+
+def fwd_workspace_bytes(T: int, M: int, Kr: int, H: int) -> int:
+    return int(lib().caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H))
+
+
+def bwd_workspace_bytes(T: int, M: int, Kr: int, H: int) -> int:
+    return int(lib().caat_pcr_bwd_workspace_bytes(T, M, Kr, H))
+
+
+def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """out[T,M,H] = partial channel-reduce of X[t] @ W[t] (see caat_pcr.h)."""
+    _require(X, "X", torch.bfloat16, 3)
+    dev = X.device
+    _require(W, "W", torch.bfloat16, 3, dev)
+    _require(mask, "mask", torch.uint8, 1, dev)
+    T, M, Kr = X.shape
+    H = W.shape[2]
+    if W.shape[0] != T or W.shape[1] != Kr or mask.shape[0] != H:
+        raise ValueError(f"shape mismatch: X{tuple(X.shape)} W{tuple(W.shape)} mask{tuple(mask.shape)}")
+    if out is None:
+        out = torch.empty((T, M, H), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != (T, M, H):
+        raise ValueError(f"out must be {(T, M, H)}, got {tuple(out.shape)}")
+    need = fwd_workspace_bytes(T, M, Kr, H)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = _fwd_workspace(dev, need)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib().caat_rowpar_pcr_fwd(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, ws_ptr, ws_bytes,
+                                   _stream(dev))
+    _check(st, "caat_rowpar_pcr_fwd")
+    return out
+
+
+def pcr_bwd(dZ: torch.Tensor, X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor,
+            dX: torch.Tensor | None = None, dW: torch.Tensor | None = None,
+            need_dx: bool = True, need_dw: bool = True, workspace: torch.Tensor | None = None):
+    """(dX[T,M,Kr], dW[T,Kr,H]) for incoming per-rank gradients dZ[T,M,H]."""
+    _require(dZ, "dZ", torch.bfloat16, 3)
+    dev = dZ.device
+    _require(X, "X", torch.bfloat16, 3, dev)
+    _require(W, "W", torch.bfloat16, 3, dev)
+    _require(mask, "mask", torch.uint8, 1, dev)
+    T, M, H = dZ.shape
+    Kr = X.shape[2]
+    if tuple(X.shape) != (T, M, Kr) or tuple(W.shape) != (T, Kr, H) or mask.shape[0] != H:
+        raise ValueError(f"shape mismatch: dZ{tuple(dZ.shape)} X{tuple(X.shape)} W{tuple(W.shape)}")
+    if need_dx and dX is None:
+        dX = torch.empty((T, M, Kr), dtype=torch.bfloat16, device=dev)
+    if need_dw and dW is None:
+        dW = torch.empty((T, Kr, H), dtype=torch.bfloat16, device=dev)
+    if dX is not None:
+        _require(dX, "dX", torch.bfloat16, 3, dev)
+    if dW is not None:
+        _require(dW, "dW", torch.bfloat16, 3, dev)
+    need = bwd_workspace_bytes(T, M, Kr, H)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().caat_pcr_bwd(_ptr(dZ), _ptr(X), _ptr(W), _ptr(mask), _ptr(dX), _ptr(dW), T, M, Kr, H,
+                            _ptr(workspace), ws_bytes, _stream(dev))
+    _check(st, "caat_pcr_bwd")
+    return dX, dW
+
+
+def partial_channel_reduce(Y: torch.Tensor, mask: torch.Tensor, out: torch.Tensor | None = None,
+                           inplace: bool = False) -> torch.Tensor:
+    """The reduce alone on per-rank Y[T,M,H] (float32 or bfloat16)."""
+    if Y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("Y must be float32 or bfloat16")
+    _require(Y, "Y", Y.dtype, 3)
+    dev = Y.device
+    _require(mask, "mask", torch.uint8, 1, dev)
+    T, M, H = Y.shape
+    if mask.shape[0] != H:
+        raise ValueError("mask length must equal H")
+    if inplace:
+        out = Y
+    elif out is None:
+        out = torch.empty_like(Y)
+    _require(out, "out", Y.dtype, 3, dev)
+    if out.shape != Y.shape:
+        raise ValueError("out must have Y's shape")
+    dt = CAAT_F32 if Y.dtype == torch.float32 else CAAT_BF16
+    st = lib().caat_partial_channel_reduce(_ptr(Y), _ptr(mask), _ptr(out), T, M, H, dt, _stream(dev))
+    _check(st, "caat_partial_channel_reduce")
+    return out

@@ -106,11 +106,16 @@ def make_reduce_input(T: int, M: int, H: int, seed: int = 0, dtype: str = "f32")
     return rng.standard_normal((T, M, H), dtype=np.float32)
 
 
-def make_integer_fwd_inputs(T: int, M: int, Kr: int, H: int, seed: int = 0, lo: int = -2, hi: int = 2):
-    """Small-integer X, W (exact in bf16; every product and partial sum is an
-    integer far below 2**8, so any summation order gives the same bits)."""
+def make_integer_fwd_inputs(T: int, M: int, Kr: int, H: int, seed: int = 0, lo: int = -2, hi: int = 2,
+                            x_zero_frac: float = 0.0):
+    """Small-integer X, W (exact in bf16).  With few enough nonzero products
+    every partial sum stays an integer below 2**8, so any summation order gives
+    the same bits; x_zero_frac zeroes that fraction of X to keep long
+    contractions in range."""
     rng = np.random.default_rng(seed + 40_000)
     X = rng.integers(lo, hi + 1, size=(T, M, Kr)).astype(np.float32)
+    if x_zero_frac > 0:
+        X *= (rng.random((T, M, Kr)) >= x_zero_frac).astype(np.float32)
     W = rng.integers(lo, hi + 1, size=(T, Kr, H)).astype(np.float32)
     return f32_to_bf16_bits(X), f32_to_bf16_bits(W)
 

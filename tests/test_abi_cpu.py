@@ -1,0 +1,170 @@
+"""CPU: the C-ABI library loads, exports every symbol the header declares, and
+rejects invalid arguments on the host before any GPU work (no GPU needed)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from partial_channel_reduce_amd import build as pbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "caat_pcr.h")
+
+OK, NULL, DIM, ALIGN, ALIAS, DTYPE, WS, LAUNCH = range(8)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pbuild.LIBPATH):
+        pbuild.build()
+    from partial_channel_reduce_amd import ops
+
+    return ops.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(caat_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("caat_rowpar_pcr_fwd", "caat_pcr_bwd", "caat_partial_channel_reduce"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from partial_channel_reduce_amd import ops
+
+    declared = header_functions()
+    assert sorted(n for n, _, _ in ops.SIGNATURES) == declared
+    for n in declared:
+        assert hasattr(L, n), n
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", pbuild.LIBPATH], capture_output=True, text=True).stdout
+        exported = set(re.findall(r"\sT\s(caat_\w+)", out))
+        assert set(declared) <= exported
+
+
+def test_status_strings(L):
+    assert L.caat_abi_version() == 1
+    for s in range(8):
+        assert L.caat_status_string(s).decode()
+    assert L.caat_status_string(99).decode() == "unknown status"
+
+
+# Fake but well-aligned device addresses: validation never dereferences them.
+A = 0x7F0000000000
+B = 0x7F0100000000
+C = 0x7F0200000000
+D = 0x7F0300000000
+E = 0x7F0400000000
+
+
+def fwd(L, X=A, W=B, mask=C, out=D, T=8, M=64, Kr=64, H=64, ws=None, wsb=0):
+    return L.caat_rowpar_pcr_fwd(X, W, mask, out, T, M, Kr, H, ws, wsb, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, X=None) == NULL
+    assert fwd(L, W=None, M=0) == NULL
+    assert fwd(L, X=None, out=None, M=0) == OK  # empty tensors may be NULL
+    assert fwd(L, mask=None) == NULL
+    assert fwd(L, T=0) == DIM
+    assert fwd(L, T=65) == DIM
+    assert fwd(L, M=-1) == DIM
+    assert fwd(L, Kr=12) == DIM
+    assert fwd(L, H=100) == DIM
+    assert fwd(L, Kr=0) == DIM
+    assert fwd(L, X=A + 8) == ALIGN
+    assert fwd(L, out=D + 2) == ALIGN
+    assert fwd(L, mask=C + 4) == ALIGN
+    assert fwd(L, out=A) == ALIAS  # out over X
+    assert fwd(L, out=B + 16) == ALIAS  # out over W
+    # per-rank slice beyond 32-bit element offsets
+    assert fwd(L, T=1, M=1 << 20, Kr=4096, H=64) == DIM
+    # decode-shaped call without its workspace
+    assert fwd(L, M=8) == WS
+    need = L.caat_rowpar_pcr_fwd_workspace_bytes(8, 8, 64, 64)
+    assert need > 0
+    assert fwd(L, M=8, ws=E, wsb=need - 4) == WS
+    assert fwd(L, M=8, ws=E + 16, wsb=need) == WS  # workspace must be 256-byte aligned
+    assert fwd(L, M=8, ws=D, wsb=need) == ALIAS  # workspace over out
+    # empty input: nothing to do, nothing enqueued
+    assert fwd(L, M=0) == OK
+
+
+def test_workspace_sizes(L):
+    T, Kr, H = 8, 1376, 4096
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 33, Kr, H) == 0  # tiled path needs none
+    for M in (1, 8, 32):
+        need = L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H)
+        assert need >= T * M * H * 4 + (H // 64) * 4
+        assert need % 256 == 0
+    assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) >= 16384 * H * 2
+    assert L.caat_pcr_bwd_workspace_bytes(T, 0, Kr, H) == 0
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(0, 8, Kr, H) == 0  # invalid dims report 0
+
+
+def bwd(L, dZ=A, X=B, W=C, mask=D, dX=E, dW=E + (1 << 32), T=4, M=64, Kr=64, H=64, ws=E + (2 << 32), wsb=1 << 20):
+    return L.caat_pcr_bwd(dZ, X, W, mask, dX, dW, T, M, Kr, H, ws, wsb, None)
+
+
+def test_bwd_validation(L):
+    assert bwd(L, dZ=None) == NULL
+    assert bwd(L, mask=None) == NULL
+    assert bwd(L, W=None) == NULL  # dX requested without W
+    assert bwd(L, X=None) == NULL  # dW requested without X
+    assert bwd(L, H=12) == DIM
+    assert bwd(L, dX=E + 4) == ALIGN
+    assert bwd(L, dX=A) == ALIAS  # dX over dZ
+    assert bwd(L, dW=E) == ALIAS  # dW over dX
+    assert bwd(L, ws=None) == WS
+    assert bwd(L, wsb=16) == WS
+    assert bwd(L, ws=A) == ALIAS  # workspace over dZ
+    assert bwd(L, dX=None, dW=None) == OK  # nothing requested: nothing enqueued
+    assert bwd(L, M=0, dW=None) == OK  # empty input, dX empty
+
+
+def test_reduce_validation(L):
+    red = L.caat_partial_channel_reduce
+    assert red(None, C, D, 8, 16, 64, 0, None) == NULL
+    assert red(A, None, D, 8, 16, 64, 0, None) == NULL
+    assert red(None, C, None, 8, 0, 64, 0, None) == OK
+    assert red(A, C, D, 8, 16, 64, 7, None) == DTYPE
+    assert red(A, C, D, 0, 16, 64, 0, None) == DIM
+    assert red(A, C, D, 8, 16, 60, 0, None) == DIM
+    assert red(A + 4, C, D, 8, 16, 64, 0, None) == ALIGN
+    assert red(A, C, A + 256, 8, 16, 64, 0, None) == ALIAS  # partial overlap
+    assert red(A, C, D, 8, 0, 64, 0, None) == OK  # empty
+    assert red(A, C, A, 8, 0, 64, 1, None) == OK  # in place, empty
+
+
+def test_workspace_init_validation(L):
+    assert L.caat_workspace_init(None, 16, None) == NULL
+    assert L.caat_workspace_init(A, 6, None) == ALIGN
+    assert L.caat_workspace_init(None, 0, None) == OK
+
+
+def test_product_path_fails_loudly_without_library(tmp_path):
+    """No silent fallback: a missing library raises."""
+    from partial_channel_reduce_amd import ops
+
+    with pytest.raises(RuntimeError, match="not built"):
+        ops.lib(str(tmp_path / "missing.so"))
+
+
+def test_binding_signatures_match_header_arity():
+    from partial_channel_reduce_amd import ops
+
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, _, args in ops.SIGNATURES:
+        m = re.search(name + r"\s*\(([^)]*)\)", text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), name
