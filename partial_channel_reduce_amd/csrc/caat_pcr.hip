@@ -40,7 +40,7 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 template <int BM, int BN>
 int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
                int H, hipStream_t s) {
-  const int tm = (M + BM - 1) / BM, tn = (H + BN - 1) / BN;
+  const int tm = (H + BM - 1) / BM, tn = (M + BN - 1) / BN;  // channel tiles x token tiles
   hipLaunchKernelGGL((rowpar_pcr_fwd_kernel<BM, BN>), dim3(tm * tn), dim3(kGemmThreads), 0, s, X, W, mask, out, T,
                      M, Kr, H, tm, tn);
   return launched();
@@ -49,7 +49,7 @@ int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
 template <int BM, int BN>
 int launch_dx(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* W, const uint8_t* mask, uint16_t* dX, int T,
               int M, int Kr, int H, hipStream_t s) {
-  const int tm = (M + BM - 1) / BM, tn = (Kr + BN - 1) / BN;
+  const int tm = (Kr + BM - 1) / BM, tn = (M + BN - 1) / BN;  // dX column tiles x token tiles
   hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, dZ, Gs, W, mask, dX,
                      T, M, Kr, H, tm, tn);
   return launched();
@@ -58,7 +58,7 @@ int launch_dx(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* W, const u
 template <int BM, int BN>
 int launch_dw(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* X, const uint8_t* mask, uint16_t* dW, int T,
               int M, int Kr, int H, hipStream_t s) {
-  const int tm = (Kr + BM - 1) / BM, tn = (H + BN - 1) / BN;
+  const int tm = (H + BM - 1) / BM, tn = (Kr + BN - 1) / BN;  // channel tiles x dW row tiles
   hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, dZ, Gs, X, mask, dW,
                      T, M, Kr, H, tm, tn);
   return launched();
@@ -118,6 +118,7 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
                        counters, partial, T, M, Kr, H);
     return launched();
   }
+  if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256>(X, W, mask, out, T, M, Kr, H, s);
   return launch_fwd<128, 128>(X, W, mask, out, T, M, Kr, H, s);
 }
 

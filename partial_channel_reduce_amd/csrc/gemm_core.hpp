@@ -1,15 +1,23 @@
 // bf16 MFMA GEMM building blocks for gfx950 (CDNA4).
 //
 // A workgroup of 256 threads (4 wave64s in a 2x2 grid) owns a BM x BN output
-// tile and walks the contraction in 64-wide chunks.  Each chunk of both
-// operands is staged through LDS as [row][64 k] bf16 rows (see lds_off), double
-// buffered, with the next chunk's global loads in flight while the current one
-// feeds v_mfma_f32_32x32x16_bf16 (fp32 accumulation).
+// tile and walks the contraction in 64-wide chunks, double buffered in LDS.
+// Each wave accumulates its (BM/2) x (BN/2) sub-tile with
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).
 //
-// Operands are described by where their contraction index is contiguous:
-//   * KCONT:  memory [row][k], k contiguous  -> 16-byte vectors copied as is;
-//   * MNCONT: memory [k][row], row contiguous -> 8x8 blocks loaded as 8 rows of
-//             16 bytes and transposed in registers before the LDS write.
+// Operands are described by where their contraction index k is contiguous in
+// global memory, and each kind keeps that orientation in LDS:
+//   * KCONT  [row][k]: LDS tile [R rows][64 k], 128 B rows, 16-byte chunks XOR
+//            swizzled by row; an MFMA fragment (8 consecutive k of one row) is
+//            one ds_read_b128.
+//   * MNCONT [k][row]: LDS tile [64 k][R rows], 2R-byte rows, 16-byte chunks
+//            XOR swizzled by k; a fragment is gathered and transposed by two
+//            ds_read_b64_tr_b16 (gfx950's LDS transpose read: within each
+//            16-lane group, lane 4s+u names 4 consecutive rows of k-row s, and
+//            every lane receives one row's values from the 4 k-rows).
+// Plain operands are copied global -> LDS with global_load_lds_dwordx4 (no
+// register staging); operands that need a per-element select are staged
+// through registers and written with ds_write_b128.
 #pragma once
 
 #include "common.hpp"
@@ -19,105 +27,134 @@ namespace caat {
 constexpr int kGemmThreads = 256;
 constexpr int kBK = 64;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
 template <int BM, int BN>
 struct TileShape {
   static constexpr int WM = BM / 2, WN = BN / 2;    // per-wave sub-tile (2x2 waves)
   static constexpr int WI = WM / 32, WJ = WN / 32;  // 32x32 MFMA blocks per wave
-  static constexpr int LDS_ELEMS = 2 * (BM + BN) * kBK;  // double buffer, bf16 elements
+  static constexpr int BUF = (BM + BN) * kBK;       // one stage, bf16 elements
+  static constexpr int LDS_ELEMS = 2 * BUF;         // double buffer
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
 };
 
-// ---- KCONT loader: R rows x 64 k, one 16-byte vector per (row, k-chunk) -------
-template <int R>
-struct KContLoader {
-  static constexpr int NV = (R * 8 + kGemmThreads - 1) / kGemmThreads;
-  u32x4 v[NV];
-
-  // src(row, k) returns the 16-byte vector of 8 k-values at (row, k..k+7) or
-  // zero; the caller clamps rows and zero-fills k beyond the contraction.
-  template <class Src>
-  __device__ __forceinline__ void load(Src&& src, int tid) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int q = tid + i * kGemmThreads;
-      if (R * 8 % kGemmThreads == 0 || q < R * 8) v[i] = src(q >> 3, (q & 7) * 8);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int q = tid + i * kGemmThreads;
-      if (R * 8 % kGemmThreads == 0 || q < R * 8) st16(lds + lds_off(q >> 3, q & 7), v[i]);
-    }
-  }
-};
-
-// ---- MNCONT loader: 64 k x R rows held as [k][row]; 8x8 blocks per thread -----
-template <int R>
-struct MNContLoader {
-  static constexpr int NBLK = (kBK / 8) * (R / 8);
-  static constexpr int NB = (NBLK + kGemmThreads - 1) / kGemmThreads;
-  u32x4 v[NB][8];
-
-  // src(kk, row) returns 8 consecutive rows' values at contraction index kk
-  // (16 bytes), or zero beyond the contraction.
-  template <class Src>
-  __device__ __forceinline__ void load(Src&& src, int tid) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int q = tid + b * kGemmThreads;
-      if (NBLK % kGemmThreads == 0 || q < NBLK) {
-        const int rb = q % (R / 8), kb = q / (R / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[b][i] = src(kb * 8 + i, rb * 8);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int q = tid + b * kGemmThreads;
-      if (NBLK % kGemmThreads == 0 || q < NBLK) {
-        const int rb = q % (R / 8), kb = q / (R / 8);
-        u32x4 o[8];
-        transpose8x8(v[b], o);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st16(lds + lds_off(rb * 8 + j, kb), o[j]);
-      }
-    }
-  }
-};
+// Accumulators of one wave: WI x WJ blocks of 32x32 fp32.
+template <int BM, int BN>
+using AccTile = f32x16[TileShape<BM, BN>::WI][TileShape<BM, BN>::WJ];
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// One 64-wide chunk of MFMAs for this wave's WI x WJ blocks.
-template <int BM, int BN>
-__device__ __forceinline__ void mma_chunk(const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane,
-                                          f32x16 (&acc)[TileShape<BM, BN>::WI][TileShape<BM, BN>::WJ]) {
-  using S = TileShape<BM, BN>;
-  const int r = lane & 31;
+// ---- LDS layouts ----------------------------------------------------------------
+// KCONT: element offset of 16-byte chunk `chunk` (0..7) of row `row`.  XOR with
+// row % 8 keeps the 32 rows of an MFMA fragment read on distinct banks.
+__device__ __forceinline__ int kc_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// MNCONT with R elements per k-row: element offset of logical chunk `chunk`
+// (0..R/8-1) of k-row `k`.  The swizzle keeps chunk pairs (2c, 2c+1) adjacent
+// and spreads 4 consecutive k-rows over distinct banks.
+template <int R>
+__device__ __forceinline__ int mn_off(int k, int chunk) { return k * R + ((chunk ^ ((k & 3) << 1)) << 3); }
+
+// ---- direct global -> LDS copies (one wave instruction moves 1 KiB) -------------
+// Buffer loads with an LDS destination.  The per-lane part of the address is
+// the same for every instruction of a tile (one VGPR), the rest is a uniform
+// SGPR offset; reads past the end of the buffer return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+
+// KCONT tile: rows r0..r0+R-1 of a row-major [rows][ld] buffer, k0..k0+63.
+// Rows past the buffer read as zero; k past the contraction reads the next
+// row's values, which the caller clears (zero_kcont_tail).
+struct KcDma {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff;  // bytes: this lane's (row in group of 8, swizzled chunk)
+  __device__ __forceinline__ KcDma(const void* base, uint32_t nbytes, int ld, int lane) {
+    rsrc = make_rsrc(base, nbytes);
+    const int r = lane >> 3;
+    voff = (r * ld + (((lane & 7) ^ r) << 3)) * 2;
+  }
+  template <int R>
+  __device__ __forceinline__ void load(int ld, int r0, int k0, uint16_t* tile, int wave) const {
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) {
-    const int kc = ks * 2 + (lane >> 5);
-    u32x4 a[S::WI], b[S::WJ];
+    for (int i = 0; i < R / 32; ++i) {
+      const int rb = (i * 4 + wave) * 8;  // 8 rows per instruction
+      const int soff = ((r0 + rb) * ld + k0) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + rb * kBK), 16, voff, soff, 0, 0);
+    }
+  }
+};
+
+// MNCONT tile: k-rows k0..k0+63 of a row-major [k][ld] buffer, columns
+// c0..c0+R-1.  k-rows past the buffer read as zero.
+template <int R>
+struct MnDma {
+  static constexpr int CPR = R / 8;     // 16-byte chunks per k-row
+  static constexpr int RPI = 64 / CPR;  // k-rows per instruction
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff;
+  __device__ __forceinline__ MnDma(const void* base, uint32_t nbytes, int ld, int lane, int wave) {
+    rsrc = make_rsrc(base, nbytes);
+    const int kr = lane / CPR;                 // k-row within the instruction
+    const int k = (wave * RPI + kr) & 3;       // (row in tile) % 4, the same for every instruction
+    const int chunk = (lane % CPR) ^ (k << 1);  // logical chunk stored at this lane's slot
+    voff = (kr * ld + chunk * 8) * 2;
+  }
+  __device__ __forceinline__ void load(int ld, int c0, int k0, uint16_t* tile, int wave) const {
 #pragma unroll
-    for (int i = 0; i < S::WI; ++i) a[i] = ld16(As + lds_off(wm * S::WM + i * 32 + r, kc));
-#pragma unroll
-    for (int j = 0; j < S::WJ; ++j) b[j] = ld16(Bs + lds_off(wn * S::WN + j * 32 + r, kc));
-#pragma unroll
-    for (int i = 0; i < S::WI; ++i)
-#pragma unroll
-      for (int j = 0; j < S::WJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]), acc[i][j], 0, 0, 0);
+    for (int i = 0; i < R / 32; ++i) {
+      const int kb = (i * 4 + wave) * RPI;
+      const int soff = ((k0 + kb) * ld + c0) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + kb * R), 16, voff, soff, 0, 0);
+    }
+  }
+};
+
+// Zero the part of a staged KCONT chunk that lies beyond the contraction
+// (k >= kvalid within the chunk).  Called after the chunk has landed and
+// before it is read.
+template <int R>
+__device__ __forceinline__ void zero_kcont_tail(uint16_t* tile, int kvalid, int tid) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const int c0 = kvalid >> 3;  // first 16-byte chunk to clear (kvalid % 8 == 0)
+  for (int q = tid; q < R * 8; q += kGemmThreads) {
+    const int row = q >> 3, c = q & 7;
+    if (c >= c0) st16(tile + kc_off(row, c), z);
   }
 }
 
-// Row (within the 32x32 block) of accumulator register e of lane `lane`; the
-// column is lane % 32.
+// ---- fragments ------------------------------------------------------------------
+// KCONT fragment of 32 rows starting at rb, k16 step ks: lane l gets row rb+l%32,
+// k = ks*16 + 8*(l/32) .. +7.
+__device__ __forceinline__ u32x4 frag_kcont(const uint16_t* tile, int rb, int ks, int lane) {
+  return ld16(tile + kc_off(rb + (lane & 31), ks * 2 + (lane >> 5)));
+}
+// MNCONT fragment of 32 rows starting at rb: same lane layout as frag_kcont,
+// gathered from the [k][R] tile by two transpose reads.
+template <int R>
+__device__ __forceinline__ u32x4 frag_mncont(const uint16_t* tile, int rb, int ks, int lane) {
+  const int g = lane >> 4, jj = lane & 15, s = jj >> 2, u = jj & 3;
+  const int col = rb + 16 * (g & 1) + 4 * u;  // first of the 4 rows this lane names
+  const int kbase = ks * 16 + 8 * (g >> 1) + s;
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = kbase + 4 * h;
+    const int off = mn_off<R>(k, col >> 3) + (col & 7);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + off));
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    r[2 * h] = w[0];
+    r[2 * h + 1] = w[1];
+  }
+  return r;
+}
+
+// Row (within a 32x32 block) of accumulator register e of `lane`; the column is lane % 32.
 __device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
 
-// Grouped raster of a tiles_m x tiles_n grid: GROUP m-tiles are walked
-// column by column, so consecutive tiles share B columns and nearby A rows.
+// Grouped raster of a tiles_m x tiles_n grid: GROUP m-tiles are walked column
+// by column, so tiles running together share B columns and nearby A rows.
 __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
@@ -129,60 +166,44 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
   tn = in / gsz;
 }
 
-// The double-buffered main loop.  load(c) issues chunk c's global loads into
-// registers, store(a_lds, b_lds) writes them to LDS; after chunk c's MFMAs,
-// after_chunk(c) runs (the forward uses it at rank boundaries).
-template <int BM, int BN, class Load, class Store, class After>
-__device__ __forceinline__ void gemm_mainloop(uint16_t* smem, int nchunks, Load&& load, Store&& store,
-                                              After&& after_chunk,
-                                              f32x16 (&acc)[TileShape<BM, BN>::WI][TileShape<BM, BN>::WJ]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  constexpr int BUF = (BM + BN) * kBK;
-  if (nchunks <= 0) return;
-  load(0);
-  store(smem, smem + BM * kBK);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    uint16_t* cur = smem + (c & 1) * BUF;
-    uint16_t* nxt = smem + ((c + 1) & 1) * BUF;
-    const bool more = c + 1 < nchunks;
-    if (more) load(c + 1);
-    mma_chunk<BM, BN>(cur, cur + BM * kBK, wm, wn, lane, acc);
-    if (more) store(nxt, nxt + BM * kBK);
-    after_chunk(c);
-    __syncthreads();
-  }
+template <int BM, int BN>
+__device__ __forceinline__ void zero_acc(AccTile<BM, BN>& acc) {
+#pragma unroll
+  for (int i = 0; i < TileShape<BM, BN>::WI; ++i)
+#pragma unroll
+    for (int j = 0; j < TileShape<BM, BN>::WJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-
-// Forward variant of the main loop: the contraction is T ranks of nk chunks.
-// Between ranks, at_rank_end(t) runs once (outside the inner chunk loop, so
-// the inner loop's accumulators stay in MFMA accumulation registers).
-template <int BM, int BN, class Load, class Store, class RankEnd>
-__device__ __forceinline__ void gemm_mainloop_ranks(uint16_t* smem, int T, int nk, Load&& load, Store&& store,
-                                                    RankEnd&& at_rank_end,
-                                                    f32x16 (&acc)[TileShape<BM, BN>::WI][TileShape<BM, BN>::WJ]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  constexpr int BUF = (BM + BN) * kBK;
-  const int nchunks = T * nk;
-  if (nchunks <= 0) return;
-  load(0);
-  store(smem, smem + BM * kBK);
-  __syncthreads();
-  int c = 0;
-  for (int t = 0; t < T; ++t) {
-    for (int kc = 0; kc < nk; ++kc, ++c) {
-      uint16_t* cur = smem + (c & 1) * BUF;
-      uint16_t* nxt = smem + ((c + 1) & 1) * BUF;
-      const bool more = c + 1 < nchunks;
-      if (more) load(c + 1);
-      mma_chunk<BM, BN>(cur, cur + BM * kBK, wm, wn, lane, acc);
-      if (more) store(nxt, nxt + BM * kBK);
-      __syncthreads();
+// One 64-wide chunk of MFMAs.  Fragments for k16 step ks+1 are read before the
+// MFMAs of step ks are issued, so LDS latency hides behind 16 MFMAs.
+// fa(ks, i) / fb(ks, j) return the A / B fragments of block i / j.
+template <int BM, int BN, class FA, class FB>
+__device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN>& acc) {
+  using S = TileShape<BM, BN>;
+  u32x4 a[2][S::WI], b[2][S::WJ];
+#pragma unroll
+  for (int i = 0; i < S::WI; ++i) a[0][i] = fa(0, i);
+#pragma unroll
+  for (int j = 0; j < S::WJ; ++j) b[0][j] = fb(0, j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) {
+    if (ks + 1 < kBK / 16) {
+#pragma unroll
+      for (int i = 0; i < S::WI; ++i) a[(ks + 1) & 1][i] = fa(ks + 1, i);
+#pragma unroll
+      for (int j = 0; j < S::WJ; ++j) b[(ks + 1) & 1][j] = fb(ks + 1, j);
     }
-    if (t + 1 < T) at_rank_end(t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+      for (int j = 0; j < S::WJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[ks & 1][i]), as_bf16x8(b[ks & 1][j]),
+                                                            acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
