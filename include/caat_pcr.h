@@ -72,10 +72,9 @@ const char* caat_status_string(int status);
  *   out[t][:, c] = sum_u Y_u[:, c]     for c in S   (same value on every rank)
  *   out[t][:, c] = Y_t[:, c]           for c not in S
  * rounded once to bf16 (nearest even).  `out` must not overlap X, W or mask.
- * M <= 32 (decode-shaped calls) uses a weight-streaming kernel that needs
- * caat_rowpar_pcr_fwd_workspace_bytes() bytes of workspace, zero-filled before
- * its first use (caat_workspace_init); each call leaves it zero-filled again.
- * Other M need no workspace (pass NULL, 0).
+ * Decode-shaped calls (M <= 32) run a weight-streaming kernel pair that needs
+ * caat_rowpar_pcr_fwd_workspace_bytes() bytes of workspace (fp32 partials of
+ * the synced channels; any contents); other M need none (pass NULL, 0).
  */
 int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out,
                         int T, int M, int Kr, int H,
@@ -108,9 +107,6 @@ size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H);
  */
 int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out,
                                 int T, int M, int H, int dtype, void* stream);
-
-/* Zero-fill `bytes` of workspace on `stream` (bytes a multiple of 4). */
-int caat_workspace_init(void* workspace, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -91,7 +91,7 @@ const char* caat_status_string(int status) {
 
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0 || M > kDecMaxM) return 0;
-  return dec_counter_bytes(H) + round256((size_t)T * M * H * sizeof(float));
+  return round256((size_t)T * M * H * sizeof(float));
 }
 
 int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M,
@@ -101,21 +101,25 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
   if (!W || !mask || (M > 0 && (!X || !out))) return CAAT_ERR_NULL;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(out, 16) || !aligned(mask, 8)) return CAAT_ERR_ALIGN;
   const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nO = (size_t)T * M * H * 2;
-  if (overlap(out, nO, X, nX) || overlap(out, nO, W, nW) || overlap(out, nO, mask, H)) return CAAT_ERR_ALIAS;
+  if (M > 0 && (overlap(out, nO, X, nX) || overlap(out, nO, W, nW) || overlap(out, nO, mask, H))) return CAAT_ERR_ALIAS;
   const size_t need = caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H);
   if (need > 0) {
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return CAAT_ERR_WORKSPACE;
-    if (overlap(workspace, need, out, nO) || overlap(workspace, need, X, nX) || overlap(workspace, need, W, nW))
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return CAAT_ERR_WORKSPACE;
+    if (overlap(workspace, need, out, nO) || overlap(workspace, need, X, nX) || overlap(workspace, need, W, nW) ||
+        overlap(workspace, need, mask, H))
       return CAAT_ERR_ALIAS;
   }
   if (M == 0) return CAAT_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (M <= kDecMaxM) {
-    uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
-    float* partial = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + dec_counter_bytes(H));
-    const int nblocks = (H + kDecBN - 1) / kDecBN;
-    hipLaunchKernelGGL(rowpar_pcr_decode_kernel, dim3(nblocks * T), dim3(kGemmThreads), 0, s, X, W, mask, out,
-                       counters, partial, T, M, Kr, H);
+    float* partial = static_cast<float*>(workspace);
+    const dim3 grid(((H + kDecCols - 1) / kDecCols) * T);
+    if (M <= 16)
+      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, T, M, Kr, H);
+    else
+      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<2>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, T, M, Kr, H);
+    if (int st = launched()) return st;
+    hipLaunchKernelGGL(decode_sync_sum_kernel, dim3((M * H + 255) / 256), dim3(256), 0, s, partial, mask, out, T, M, H);
     return launched();
   }
   if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256>(X, W, mask, out, T, M, Kr, H, s);
@@ -163,9 +167,9 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
     return CAAT_OK;
   }
   uint16_t* Gs = reinterpret_cast<uint16_t*>(workspace);
-  const long long nvec = (long long)M * (H / 8);
-  hipLaunchKernelGGL(grad_sync_sum_kernel, dim3((unsigned)((nvec + kReduceThreads - 1) / kReduceThreads)),
-                     dim3(kReduceThreads), 0, s, dZ, mask, Gs, T, nvec, H / 8, (long long)M * H);
+  const uint32_t nvec = (uint32_t)((long long)M * (H / 8));
+  hipLaunchKernelGGL(grad_sync_sum_kernel, dim3((nvec + kReduceThreads - 1) / kReduceThreads), dim3(kReduceThreads),
+                     0, s, dZ, mask, Gs, T, nvec, (uint32_t)(H / 8), (long long)M * H);
   if (int st = launched()) return st;
   if (dX) {
     const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256>(dZ, Gs, W, mask, dX, T, M, Kr, H, s)
@@ -196,34 +200,33 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const long long mh = (long long)M * H;
   if (dtype == CAAT_F32) {
-    const long long nvec = mh / 4;
-    const dim3 grid((unsigned)((nvec + kReduceThreads - 1) / kReduceThreads));
+    const uint32_t nvec = (uint32_t)(mh / 4);
+    const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
     const float* y = static_cast<const float*>(Y);
     float* o = static_cast<float*>(out);
     const int ip = inplace ? 1 : 0;
+    const uint32_t hv = (uint32_t)(H / 4);
     switch (T) {
-      case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
-      case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
-      case 4: hipLaunchKernelGGL(pcr_reduce_f32_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
-      case 8: hipLaunchKernelGGL(pcr_reduce_f32_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
-      default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, H / 4, mh, ip); break;
+      case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      case 4: hipLaunchKernelGGL(pcr_reduce_f32_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      case 8: hipLaunchKernelGGL(pcr_reduce_f32_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
     }
   } else {
-    const long long nvec = mh / 8;
-    const dim3 grid((unsigned)((nvec + kReduceThreads - 1) / kReduceThreads));
-    hipLaunchKernelGGL(pcr_reduce_bf16_kernel, grid, dim3(kReduceThreads), 0, s, static_cast<const uint16_t*>(Y),
-                       mask, static_cast<uint16_t*>(out), T, nvec, H / 8, mh, inplace ? 1 : 0);
+    const uint32_t nvec = (uint32_t)(mh / 8);
+    const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
+    const uint16_t* y = static_cast<const uint16_t*>(Y);
+    uint16_t* o = static_cast<uint16_t*>(out);
+    const int ip = inplace ? 1 : 0;
+    const uint32_t hv = (uint32_t)(H / 8);
+    switch (T) {
+      case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+    }
   }
-  return launched();
-}
-
-int caat_workspace_init(void* workspace, size_t bytes, void* stream) {
-  if (bytes == 0) return CAAT_OK;
-  if (!workspace) return CAAT_ERR_NULL;
-  if (!aligned(workspace, 4) || bytes % 4 != 0) return CAAT_ERR_ALIGN;
-  const long long n = (long long)(bytes / 4);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace), n, 0u);
   return launched();
 }
 

@@ -80,7 +80,7 @@ struct KcDma {
 #pragma unroll
     for (int i = 0; i < R / 32; ++i) {
       const int rb = (i * 4 + wave) * 8;  // 8 rows per instruction
-      const int soff = ((r0 + rb) * ld + k0) * 2;
+      const int soff = __builtin_amdgcn_readfirstlane(((r0 + rb) * ld + k0) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + rb * kBK), 16, voff, soff, 0, 0);
     }
   }
@@ -105,7 +105,7 @@ struct MnDma {
 #pragma unroll
     for (int i = 0; i < R / 32; ++i) {
       const int kb = (i * 4 + wave) * RPI;
-      const int soff = ((k0 + kb) * ld + c0) * 2;
+      const int soff = __builtin_amdgcn_readfirstlane(((k0 + kb) * ld + c0) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + kb * R), 16, voff, soff, 0, 0);
     }
   }

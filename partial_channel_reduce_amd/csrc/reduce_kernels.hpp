@@ -16,33 +16,24 @@ namespace caat {
 constexpr int kReduceThreads = 256;
 
 // ---- fp32: one thread per 4-channel, 16-byte vector ---------------------------
-
+// Every lane of a wave takes the same path whatever its mask bytes (a lane
+// with only local channels still loads and stores its T vectors), so no lane
+// serialises the wave's loads behind a divergent branch.  In place, lanes with
+// no synced channel leave at once, and mixed vectors write synced channels only.
 template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* out,
-                      int T_rt, long long nvec, int hvec, long long mh, int inplace) {
+                      int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace) {
   const int T = TC > 0 ? TC : T_rt;
-  const long long v = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+  const uint32_t v = blockIdx.x * kReduceThreads + threadIdx.x;
   if (v >= nvec) return;
   const int c = (int)(v % hvec) * 4;
-  const long long m = v / hvec;
-  const long long base = m * (long long)hvec * 4 + c;  // element offset inside one rank
+  const long long base = (long long)v * 4;
   const uint32_t mk = *reinterpret_cast<const uint32_t*>(mask + c);
   const bool s0 = (mk & 0xffu) != 0, s1 = (mk & 0xff00u) != 0;
   const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
-  const bool any = s0 | s1 | s2 | s3;
   const bool all = s0 & s1 & s2 & s3;
-
-  if (!any) {  // only local channels: copy through (nothing to do in place)
-    if (!inplace) {
-      for (int t = 0; t < T; ++t) {
-        const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + t * mh + base));
-        __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(out + t * mh + base));
-      }
-    }
-    return;
-  }
-
+  if (inplace && mk == 0u) return;
   if (TC > 0) {
     // All T vectors stay in registers: T loads in flight, then T stores.
     f32x4 y[TC > 0 ? TC : 1];
@@ -55,7 +46,7 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
 #pragma unroll
     for (int t = 0; t < (TC > 0 ? TC : 1); ++t) {
       float* o = out + t * mh + base;
-      if (all || !inplace) {
+      if (!inplace || all) {
         f32x4 w;
         w.x = s0 ? s.x : y[t].x;
         w.y = s1 ? s.y : y[t].y;
@@ -71,14 +62,12 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
     }
   } else {
     // Runtime T: first pass sums, second pass writes (re-reading rank t's
-    // vector for the local channels of a mixed vector).
-    f32x4 s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + base));
+    // vector for the local channels).
+    f32x4 s = *reinterpret_cast<const f32x4*>(Y + base);
     for (int t = 1; t < T; ++t) s += *reinterpret_cast<const f32x4*>(Y + t * mh + base);
     for (int t = 0; t < T; ++t) {
       float* o = out + t * mh + base;
-      if (all) {
-        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(o));
-      } else if (!inplace) {
+      if (!inplace || all) {
         const f32x4 y = *reinterpret_cast<const f32x4*>(Y + t * mh + base);
         f32x4 w;
         w.x = s0 ? s.x : y.x;
@@ -116,40 +105,51 @@ __device__ __forceinline__ u32x4 expand_mask8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint16_t* out,
-                       int T, long long nvec, int hvec, long long mh, int inplace) {
-  const long long v = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+                       int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace) {
+  const int T = TC > 0 ? TC : T_rt;
+  constexpr int NR = TC > 0 ? TC : 1;  // ranks kept in registers
+  const uint32_t v = blockIdx.x * kReduceThreads + threadIdx.x;
   if (v >= nvec) return;
   const int c = (int)(v % hvec) * 8;
-  const long long m = v / hvec;
-  const long long base = m * (long long)hvec * 8 + c;
+  const long long base = (long long)v * 8;
   const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
-  if ((mk[0] | mk[1]) == 0u) {
-    if (!inplace)
-      for (int t = 0; t < T; ++t) st16_nt(out + t * mh + base, ld16(Y + t * mh + base));
-    return;
-  }
+  if (inplace && (mk[0] | mk[1]) == 0u) return;
   const u32x4 sel = expand_mask8(mk[0], mk[1]);
+  const bool all = (sel[0] & sel[1] & sel[2] & sel[3]) == 0xffffffffu;
+  u32x4 y[NR];
   float s[8];
-  bf16x8_to_f32(ld16(Y + base), s);
-  for (int t = 1; t < T; ++t) {
-    float f[8];
-    bf16x8_to_f32(ld16(Y + t * mh + base), f);
+  if (TC > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += f[e];
+    for (int t = 0; t < NR; ++t) y[t] = ld16(Y + t * mh + base);
+    bf16x8_to_f32(y[0], s);
+#pragma unroll
+    for (int t = 1; t < NR; ++t) {
+      float f[8];
+      bf16x8_to_f32(y[t], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += f[e];
+    }
+  } else {
+    bf16x8_to_f32(ld16(Y + base), s);
+    for (int t = 1; t < T; ++t) {
+      float f[8];
+      bf16x8_to_f32(ld16(Y + t * mh + base), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += f[e];
+    }
   }
   u32x4 sv;
 #pragma unroll
   for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
-  const bool all = (sel[0] & sel[1] & sel[2] & sel[3]) == 0xffffffffu;
+#pragma unroll 8
   for (int t = 0; t < T; ++t) {
     uint16_t* o = out + t * mh + base;
-    if (all) {
-      st16_nt(o, sv);
-    } else if (!inplace) {
-      const u32x4 y = ld16(Y + t * mh + base);
-      st16_nt(o, (sv & sel) | (y & ~sel));
+    if (!inplace || all) {
+      const u32x4 yt = TC > 0 ? y[t < NR ? t : 0] : ld16(Y + t * mh + base);
+      st16_nt(o, (sv & sel) | (yt & ~sel));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -163,12 +163,11 @@ pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint
 // the GEMM loaders, which select Gs only where the mask is set).
 __global__ void __launch_bounds__(kReduceThreads)
 grad_sync_sum_kernel(const uint16_t* __restrict__ dZ, const uint8_t* __restrict__ mask,
-                     uint16_t* __restrict__ Gs, int T, long long nvec, int hvec, long long mh) {
-  const long long v = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+                     uint16_t* __restrict__ Gs, int T, uint32_t nvec, uint32_t hvec, long long mh) {
+  const uint32_t v = blockIdx.x * kReduceThreads + threadIdx.x;
   if (v >= nvec) return;
   const int c = (int)(v % hvec) * 8;
-  const long long m = v / hvec;
-  const long long base = m * (long long)hvec * 8 + c;
+  const long long base = (long long)v * 8;
   const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
   if ((mk[0] | mk[1]) == 0u) return;
   float s[8];

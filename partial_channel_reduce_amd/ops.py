@@ -41,7 +41,6 @@ SIGNATURES = [
     ("caat_pcr_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     ("caat_pcr_bwd_workspace_bytes", _S, [_I, _I, _I, _I]),
     ("caat_partial_channel_reduce", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
-    ("caat_workspace_init", _I, [_P, _S, _P]),
 ]
 
 
@@ -106,20 +105,6 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-# Zero-filled workspaces for the decode-shaped forward, per device.  Each call
-# leaves its counters zeroed, so sequential calls on one stream may share one.
-_WS: dict = {}
-
-
-def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    key = (dev.type, dev.index)
-    ws = _WS.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        _WS[key] = ws
-    return ws
-
-
 def fwd_workspace_bytes(T: int, M: int, Kr: int, H: int) -> int:
     return int(lib().caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H))
 
@@ -145,12 +130,10 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
     if tuple(out.shape) != (T, M, H):
         raise ValueError(f"out must be {(T, M, H)}, got {tuple(out.shape)}")
     need = fwd_workspace_bytes(T, M, Kr, H)
-    ws_ptr, ws_bytes = None, 0
-    if need > 0:
-        if workspace is None:
-            workspace = _fwd_workspace(dev, need)
-        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
-    st = lib().caat_rowpar_pcr_fwd(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, ws_ptr, ws_bytes,
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().caat_rowpar_pcr_fwd(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, _ptr(workspace), ws_bytes,
                                    _stream(dev))
     _check(st, "caat_rowpar_pcr_fwd")
     return out

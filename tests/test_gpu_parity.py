@@ -142,6 +142,8 @@ INT_CASES = [
     (8, 1, 1376, 4096, "random", 0.5),   # decode path, M = 1
     (5, 7, 72, 136, "random", 0.25),     # decode path, ragged
     (1, 70, 64, 128, "random", 0.5),     # T = 1
+    (20, 5, 64, 136, "random", 0.5),     # M <= 32, T = 20
+    (3, 17, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
 ]
 
 
@@ -209,12 +211,12 @@ def test_fwd_empty(ops):
     assert ops.rowpar_pcr_fwd(X, W, mask).shape == (8, 0, 64)
 
 
-def test_decode_workspace_reused_across_calls(ops):
-    """The decode path's arrival counters are left zeroed; repeated calls with
-    different masks and inputs on one workspace stay correct."""
+def test_decode_repeated_calls(ops):
+    """Back-to-back decode-shaped calls with different masks, token counts and
+    inputs each match the oracle exactly (no state carried between calls)."""
     T, Kr, H = 8, 256, 1024
     for i, M in enumerate((32, 8, 1, 32)):
-        _announce(f"decode reuse call {i} M={M}")
+        _announce(f"decode repeated call {i} M={M}")
         X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=i, lo=-1, hi=1, x_zero_frac=0.5)
         mask = synth.make_mask(H, 0.5, "random", seed=i)
         got = G.from_dev_bf16(run_fwd(ops, X, W, mask))
