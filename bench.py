@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,out,reduce,decode (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,out,reduce,decode,copy (profiling runs)")
     return ap.parse_args()
 
 
@@ -229,12 +229,13 @@ def main():
         for Md in DEC_M:
             Xs = [randn_bf16((T, Md, KR)) for _ in range(nsets)]
             outs = [torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+            wsd = torch.empty(max(1, ops.fwd_workspace_bytes(T, Md, KR, H)), dtype=torch.uint8, device=dev)
             idx = [0]
 
             def call():
                 i = idx[0] % nsets
                 idx[0] += 1
-                ops.rowpar_pcr_fwd(Xs[i], Ws[i], mk, out=outs[i])
+                ops.rowpar_pcr_fwd(Xs[i], Ws[i], mk, out=outs[i], workspace=wsd)
 
             t = time_call(call, 60, warm=6)
             nbytes = 2.0 * (T * Md * KR + T * KR * H + T * Md * H)
@@ -242,6 +243,17 @@ def main():
             dec[f"M{Md}"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         res["decode_down_proj"] = dec
         del Ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------- copy of known size (counters)
+    if "copy" in legs:
+        # A plain 1 GiB device copy: the reference against which the HBM byte
+        # counters of the other kernels are scaled.
+        xs = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_(generator=gen)
+        ys = torch.empty_like(xs)
+        t = time_call(lambda: ys.copy_(xs), 5)
+        res["copy_1GiB_us"] = round(t * 1e3, 1)
+        del xs, ys
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------- CPU oracle leg

@@ -1,0 +1,135 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times: sampled outputs against the oracle evaluated element by
+element, plus properties that hold at any size (synced channels bitwise
+identical across ranks, run-to-run determinism, exact float32 summation order
+of the standalone reduce)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from partial_channel_reduce_amd import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+NSAMPLE = 1536
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from partial_channel_reduce_amd import ops as _ops
+
+    _ops.lib()
+    return _ops
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _samples(rng, n, *sizes):
+    return [rng.integers(0, s, size=n) for s in sizes]
+
+
+def _check_sampled_bf16(got, ref, synced, what):
+    G.check_bf16(got, ref, synced, what)
+
+
+def _gather(t, *idx):
+    """Elements of a device tensor at numpy index arrays, as bf16 bits."""
+    ii = tuple(torch.from_numpy(np.asarray(i, dtype=np.int64)).to(t.device) for i in idx)
+    return G.bf16_bits(t[ii])
+
+
+@pytest.mark.parametrize(
+    "name,T,M,Kr,H,kind",
+    [
+        ("Llama2-7B down-proj", 8, 16384, 1376, 4096, "random"),
+        ("Llama2-7B out-proj", 8, 16384, 512, 4096, "random"),
+        ("TinyLlama-1.1B down-proj", 8, 32768, 704, 2048, "strided"),
+        ("130M down-proj", 8, 8192, 384, 768, "random"),
+        ("130M out-proj", 8, 8192, 96, 768, "random"),
+    ],
+)
+def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind):
+    _announce(f"full-size fwd {name}")
+    X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=1)
+    mask = synth.make_mask(H, 0.5, kind, seed=1)
+    Xd, Wd, mk = G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask)
+    out = ops.rowpar_pcr_fwd(Xd, Wd, mk)
+    out2 = ops.rowpar_pcr_fwd(Xd, Wd, mk)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    S = torch.from_numpy(mask != 0).to(G.dev())
+    o16 = out.view(torch.int16)
+    for t in range(1, T):
+        assert torch.equal(o16[t][:, S], o16[0][:, S]), f"synced channels differ between rank 0 and {t}"
+    rng = np.random.default_rng(7)
+    ts, ms, cs = _samples(rng, NSAMPLE, T, M, H)
+    ref = oracle.fwd_at(X, W, mask, ts, ms, cs)
+    got = oracle.bf16_to_f64(_gather(out, ts, ms, cs))
+    _check_sampled_bf16(got, ref, mask[cs] != 0, f"fwd {name}")
+
+
+def test_bwd_7b_full_size_sampled(ops):
+    T, M, Kr, H = 8, 16384, 1376, 4096
+    _announce("full-size bwd Llama2-7B down-proj")
+    X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=2)
+    dZ = synth.make_grad(T, M, H, seed=2)
+    mask = synth.make_mask(H, 0.5, "random", seed=2)
+    args = (G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
+    dX, dW = ops.pcr_bwd(*args)
+    dX2, dW2 = ops.pcr_bwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.int16), dX2.view(torch.int16))
+    assert torch.equal(dW.view(torch.int16), dW2.view(torch.int16))
+    rng = np.random.default_rng(8)
+    ts, ms, ks = _samples(rng, NSAMPLE, T, M, Kr)
+    ref = oracle.bwd_dx_at(dZ, W, mask, ts, ms, ks)
+    G.check_bf16(oracle.bf16_to_f64(_gather(dX, ts, ms, ks)), ref, None, "dX 7B")
+    ts, ks, cs = _samples(rng, 256, T, Kr, H)
+    ref = oracle.bwd_dw_at(dZ, X, mask, ts, ks, cs)
+    G.check_bf16(oracle.bf16_to_f64(_gather(dW, ts, ks, cs)), ref, mask[cs] != 0, "dW 7B")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_decode_7b_full_size(ops, M):
+    """Decode-shaped forward on the 7B down-proj: complete comparison (the
+    oracle finishes these sizes quickly)."""
+    T, Kr, H = 8, 1376, 4096
+    _announce(f"full-size decode M={M}")
+    X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=3)
+    mask = synth.make_mask(H, 0.5, "random", seed=3)
+    out = ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
+    torch.cuda.synchronize()
+    bits = G.bf16_bits(out)
+    S = mask != 0
+    assert all(np.array_equal(bits[t][:, S], bits[0][:, S]) for t in range(T))
+    G.check_bf16(oracle.bf16_to_f64(bits), oracle.rowpar_pcr_fwd(X, W, mask), S[None, None, :], "decode")
+
+
+def test_reduce_f32_full_size(ops):
+    """fp32 reduce on Y[8, 16384, 4096] with a random 50% mask: sampled rows
+    bitwise against the float32 emulation of ascending-rank summation, and
+    against the fp64 oracle within 1e-4 rms."""
+    T, M, H = 8, 16384, 4096
+    _announce("full-size reduce f32")
+    Y = synth.make_reduce_input(T, M, H, seed=4)
+    mask = synth.make_mask(H, 0.5, "random", seed=4)
+    Yd = torch.from_numpy(Y).to(G.dev())
+    out = ops.partial_channel_reduce(Yd, G.to_dev_u8(mask))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(M, size=64, replace=False))
+    got = out[:, torch.from_numpy(rows).to(G.dev()), :].cpu().numpy()
+    Ys = Y[:, rows, :]
+    want = G.f32_sequential_reduce(Ys, mask)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    G.check_f32(got, oracle.partial_channel_reduce(Ys, mask), "reduce full size")
+    # in place on the same data: local channels untouched everywhere
+    ops.partial_channel_reduce(Yd, G.to_dev_u8(mask), inplace=True)
+    torch.cuda.synchronize()
+    L = torch.from_numpy(mask == 0).to(G.dev())
+    Yref = torch.from_numpy(Y).to(G.dev())
+    assert torch.equal(Yd[:, :, L].view(torch.int32), Yref[:, :, L].view(torch.int32))
+    assert torch.equal(Yd.view(torch.int32), out.view(torch.int32))
