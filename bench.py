@@ -33,6 +33,9 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 T, M, KR, H, P = 8, 16384, 1376, 4096, 0.5
 KR_OUT = 512
 DEC_M = (1, 8, 32)
+COPY_ELEMS = 1 << 28           # fp32 elements of the calibration kernel (1 GiB each way)
+COPY_KERNEL_KEY = "neg_kernel"  # substring naming torch's elementwise negation kernel
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_7b_down_proj.txt")
 
 
 def log(*a):
@@ -47,6 +50,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--only", default="", help="comma list of legs: train,out,reduce,decode,copy (profiling runs)")
+    ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
+    ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
+                         "calibrated against the copy leg's kernel, and exit")
     return ap.parse_args()
 
 
@@ -61,6 +68,12 @@ def src_hash() -> str:
 
 def main():
     args = parse()
+    if args.rocprof_stats:
+        print(rocprof_stats_summary(args.rocprof_stats))
+        return
+    if args.rocprof_traffic:
+        print(rocprof_traffic_summary(*args.rocprof_traffic))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(
@@ -161,7 +174,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(dom),
         }
         res["fwd_tflops"] = round(flops_fwd / (t_fwd * 1e-3) / 1e12, 2)
         res["bwd_tflops"] = round(2 * flops_fwd / (t_bwd * 1e-3) / 1e12, 2)
@@ -247,12 +260,15 @@ def main():
 
     # ------------------------------------------- copy of known size (counters)
     if "copy" in legs:
-        # A plain 1 GiB device copy: the reference against which the HBM byte
-        # counters of the other kernels are scaled.
-        xs = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_(generator=gen)
+        # A plain streaming kernel of known size (1 GiB read, 1 GiB written;
+        # an elementwise negation, so it is a kernel dispatch rather than a DMA
+        # copy): the reference against which the HBM byte counters of the other
+        # kernels are scaled.
+        xs = torch.empty(COPY_ELEMS, dtype=torch.float32, device=dev).uniform_(generator=gen)
         ys = torch.empty_like(xs)
-        t = time_call(lambda: ys.copy_(xs), 5)
-        res["copy_1GiB_us"] = round(t * 1e3, 1)
+        t = time_call(lambda: torch.neg(xs, out=ys), 5)
+        res["copy"] = {"bytes": 2 * COPY_ELEMS * 4, "us": round(t * 1e3, 1),
+                       "GB/s": round(2 * COPY_ELEMS * 4 / (t * 1e-3) / 1e9, 1)}
         del xs, ys
         torch.cuda.empty_cache()
 
@@ -290,9 +306,100 @@ def main():
         "out_proj": res.get("out_proj"),
         "reduce_only_f32": res.get("reduce_only_f32"),
         "decode_down_proj": res.get("decode_down_proj"),
+        "copy": res.get("copy"),
         "src": src_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` as recorded from the FETCH_SIZE and
+    WRITE_SIZE counters (calibrated), if they were taken on the current kernel
+    sources; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    cur = src_hash()
+    for ln in lines:
+        f = ln.strip().strip("`").split()
+        if len(f) >= 4 and f[0] == "traffic" and f[1] == kernel and f[2] == f"src={cur}":
+            return int(f[3].split("=")[1])
+    return None
+
+
+def _read_csv(path):
+    import csv
+
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def _short(name: str) -> str:
+    n = name.split("(")[0]
+    return n.replace("void ", "").replace("caat::", "")
+
+
+def rocprof_stats_summary(d: str) -> str:
+    """Markdown table of a `rocprofv3 --kernel-trace --stats --output-format csv` run."""
+    rows = _read_csv(_find(d, "kernel_stats.csv"))
+    out = ["| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+            _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def rocprof_traffic_summary(fetch_dir: str, write_dir: str) -> str:
+    """Per-kernel FETCH_SIZE / WRITE_SIZE averages (KiB per dispatch) and the
+    HBM bytes per launch they imply once scaled by what the same counters read
+    for the calibration kernel (known to move COPY_ELEMS*4 bytes each way)."""
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _read_csv(_find(d, "counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, _ = per_kernel(write_dir, "WRITE_SIZE")
+    copy_k = [k for k in fetch if COPY_KERNEL_KEY in k]
+    if not copy_k:
+        raise SystemExit("calibration kernel not found in the FETCH_SIZE run")
+    ck = copy_k[0]
+    known_kib = COPY_ELEMS * 4 / 1024.0
+    sf, sw = known_kib / fetch[ck], known_kib / write[ck]
+    out = [
+        f"calibration kernel: {_short(ck)} moving {COPY_ELEMS * 4} bytes each way",
+        f"FETCH_SIZE reads {fetch[ck]:.0f} KiB -> scale {sf:.4f}; WRITE_SIZE reads {write[ck]:.0f} KiB -> scale {sw:.4f}",
+        "",
+        "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
+        "|---|---|---|---|---|---|",
+    ]
+    cur = src_hash()
+    lines = []
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if k not in write:
+            continue
+        rb, wb = fetch[k] * sf * 1024, write[k] * sw * 1024
+        out.append(f"| {_short(k)} | {nf[k]} | {fetch[k]:.0f} | {write[k]:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        base = _short(k).split("<")[0]
+        if base.startswith(("rowpar_pcr", "pcr_bwd", "grad_sync", "pcr_reduce", "decode_sync")):
+            lines.append(f"`traffic {base} src={cur} bytes={int(rb + wb)} read={int(rb)} write={int(wb)}`")
+    return "\n".join(out + ["", "Machine-readable (kernel, kernel-source hash, calibrated bytes per dispatch):", ""]
+                     + [ln + "  " for ln in lines])
 
 
 def cpu_baseline(tokens: int):
