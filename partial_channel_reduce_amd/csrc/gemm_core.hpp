@@ -176,12 +176,16 @@ __device__ __forceinline__ void zero_acc(AccTile<BM, BN>& acc) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-// One 64-wide chunk of MFMAs.  Fragments for k16 step ks+1 are read before the
-// MFMAs of step ks are issued, so LDS latency hides behind 16 MFMAs.
+// One 64-wide chunk of MFMAs.  Fragments for k16 step ks+1 are read while the
+// MFMAs of step ks run, and `pre` (the next chunk's global loads) is issued
+// during step 0: the schedule alternates one MFMA with one LDS read and one
+// global load, so neither the LDS nor the load queue issues in a burst that
+// would leave the matrix core idle.
 // fa(ks, i) / fb(ks, j) return the A / B fragments of block i / j.
-template <int BM, int BN, class FA, class FB>
-__device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN>& acc) {
+template <int BM, int BN, class FA, class FB, class PRE>
+__device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN>& acc, PRE&& pre) {
   using S = TileShape<BM, BN>;
+  constexpr int NM = S::WI * S::WJ;
   u32x4 a[2][S::WI], b[2][S::WJ];
 #pragma unroll
   for (int i = 0; i < S::WI; ++i) a[0][i] = fa(0, i);
@@ -190,21 +194,64 @@ __device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN>& acc
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
+    if (ks == 0) pre();
     if (ks + 1 < kBK / 16) {
 #pragma unroll
       for (int i = 0; i < S::WI; ++i) a[(ks + 1) & 1][i] = fa(ks + 1, i);
 #pragma unroll
       for (int j = 0; j < S::WJ; ++j) b[(ks + 1) & 1][j] = fb(ks + 1, j);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < S::WI; ++i)
 #pragma unroll
       for (int j = 0; j < S::WJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[ks & 1][i]), as_bf16x8(b[ks & 1][j]),
                                                             acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+
+// ---- epilogue staging -----------------------------------------------------------
+// A wave's accumulators hold the transpose of its output sub-tile: MFMA rows
+// are the output's contiguous index, MFMA columns its row index, so a lane
+// owns 4 consecutive outputs of one row per register group.  Written straight
+// to memory that would make every store instruction touch 64 rows.  Instead
+// the sub-tile is staged in LDS as [row][WC] bf16 (16-byte chunks XOR
+// swizzled by row) and read back in row order, so each store instruction
+// writes whole 128-byte lines.
+template <int WC>  // contiguous extent of the sub-tile (elements, multiple of 64)
+struct RowStage {
+  static constexpr int CPR = WC / 8;    // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per wave instruction
+  static __device__ __forceinline__ int off(int r, int c) { return r * WC + ((c ^ (r & (CPR - 1))) << 3); }
+  // Block (i, *) of the accumulators into rows row0 .. row0+31.
+  static __device__ __forceinline__ void put(uint16_t* st, const f32x16& a, int i, int row0, int lane) {
+    const int r = row0 + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = i * 4 + q;
+      u32x2 v;
+      v[0] = pack_bf16x2(a[4 * q], a[4 * q + 1]);
+      v[1] = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
+      *reinterpret_cast<u32x2*>(st + off(r, c) + (lane >> 5) * 4) = v;
+    }
+  }
+  // Rows 0 .. nrows-1 in row order: store(r, c, v) gets chunk c of row r.
+  template <class F>
+  static __device__ __forceinline__ void drain(const uint16_t* st, int nrows, int lane, F&& store) {
+    const int rl = lane / CPR, c = lane % CPR;
+#pragma unroll 4
+    for (int r0 = 0; r0 < nrows; r0 += RPI) {
+      const int r = r0 + rl;
+      store(r, c, ld16(st + off(r, c)));
+    }
+  }
+};
 
 }  // namespace caat

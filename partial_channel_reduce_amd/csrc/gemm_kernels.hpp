@@ -8,8 +8,8 @@
 //   backward  G_t = the same reduce applied to dZ;  dX_t = G_t W_t^T;  dW_t = X_t^T G_t
 //
 // Every GEMM computes the transpose of its output tile (the MFMA row index is
-// the output's contiguous index), so each lane holds runs of 4 consecutive
-// output elements and writes them with one 8-byte store.
+// the output's contiguous index); the epilogues restage it through LDS in row
+// order and write whole lines with 16-byte stores.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -24,28 +24,23 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
-// 4 accumulator values (registers 4q..4q+3 of a block) as 4 packed bf16.
-__device__ __forceinline__ u32x2 pack4(const f32x16& a, int q) {
-  u32x2 r;
-  r[0] = pack_bf16x2(a[4 * q], a[4 * q + 1]);
-  r[1] = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
-  return r;
-}
-__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
-__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
-
+// Orders this wave's LDS writes before its following LDS reads (and keeps the
+// compiler from moving memory accesses across it).
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // ============================================================================
 // Forward.  One workgroup per (channel tile, token tile) walks the contraction
 // of all T ranks in rank order.  Synced channels keep accumulating across the
 // rank boundaries, so their fp32 accumulator ends as the sum over ranks
 // (ascending t), formed once and written to every rank: bit-identical synced
-// channels.  At the end of rank t its 4-channel groups are written to out[t]
-// (the synced lanes of a group hold a partial sum there and are rewritten at
-// the end) and the local accumulators restart from zero.  At the end, rank
-// T-1 gets whole groups; every other rank gets its groups read back, merged
-// with the synced channels, and written again.
+// channels.  At the end of rank t the tile is written to out[t] (its synced
+// positions hold a partial sum there and are overwritten at the end) and the
+// local accumulators restart from zero.  At the end the synced channels are
+// written to every rank.
 // A = W_t^T (channels x k, W is [k][c]: MNCONT); B = X_t (tokens x k: KCONT).
+// All stores are staged through LDS so that they write whole lines: at a
+// rank boundary through the LDS buffer of the chunk just consumed (the next
+// chunk is landing in the other one), at the end through all of LDS.
 // ============================================================================
 template <int BM, int BN>
 __global__ void __launch_bounds__(kGemmThreads, 1)
@@ -53,6 +48,12 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
                       const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                       int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
   using S = TileShape<BM, BN>;
+  using RS = RowStage<S::WM>;
+  constexpr int REG = S::BUF / 4;              // boundary staging per wave (elements)
+  constexpr int PASSES = S::WM * S::WN / REG;  // boundary passes over the wave's sub-tile
+  constexpr int JPP = S::WJ / PASSES;          // 32-token blocks per pass
+  static_assert(PASSES * REG == S::WM * S::WN && JPP * PASSES == S::WJ, "staging split");
+  static_assert(4 * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -60,21 +61,22 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, m0 = tn * BN;  // channel tile, token tile
+  const int chw = c0 + wm * S::WM;       // this wave's first channel
+  const int tkw = m0 + wn * S::WN;       // this wave's first token
   const int nk = (Kr + kBK - 1) / kBK;
   const int kv_last = Kr - (nk - 1) * kBK;  // valid k in a rank's last chunk
   const int nchunks = T * nk;
   const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
 
-  // Per lane: channel group q of block i starts at chan(i, q); keep[i] has bit
-  // e set when accumulator register e of block i is a synced channel.
-  const int cl = c0 + wm * S::WM + (lane >> 5) * 4;
+  // keepbits[i] has bit e set when accumulator register e of block i holds a
+  // synced channel (channel chw + i*32 + (e/4)*8 + (lane/32)*4 + e%4).
   uint32_t keepbits[S::WI];
 #pragma unroll
   for (int i = 0; i < S::WI; ++i) {
     uint32_t kb = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int ch = cl + i * 32 + q * 8;
+      const int ch = chw + (lane >> 5) * 4 + i * 32 + q * 8;
       const uint32_t m4 = ch < H ? *reinterpret_cast<const uint32_t*>(mask + ch) : 0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) kb |= ((m4 >> (8 * r)) & 0xffu) ? (1u << (4 * q + r)) : 0u;
@@ -97,8 +99,8 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 
   issue(0);
   for (int t = 0; t < T; ++t) {
-    for (int kc = 0; kc < nk; ++kc) {
-      const int c = t * nk + kc;
+    int c = t * nk;
+    for (int kc = 0; kc < nk; ++kc, ++c) {
       uint16_t* As = smem + (c & 1) * S::BUF;
       uint16_t* Bs = As + BM * kBK;
       __builtin_amdgcn_s_waitcnt(0);
@@ -107,79 +109,95 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
         zero_kcont_tail<BN>(Bs, kv_last, tid);
         __syncthreads();
       }
-      if (c + 1 < nchunks) issue(c + 1);
       mma_chunk<BM, BN>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
-                        [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc);
+                        [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                        [&] {
+                          if (c + 1 < nchunks) issue(c + 1);
+                        });
     }
-    if (t + 1 < T) {
-      // End of rank t: write its groups, then restart the local channels.
-      const int chb = opaque(cl);
-      const int tok = opaque(m0 + wn * S::WN + (lane & 31));
+    {
+      // End of rank t: stage and write the tile to out[t], restart the local
+      // channels.  The staging area is this wave's quarter of the buffer the
+      // last chunk was read from.
+      __syncthreads();
+      uint16_t* st = smem + ((c - 1) & 1) * S::BUF + wave * REG;
       uint16_t* ot = out + t * MH;
 #pragma unroll
-      for (int i = 0; i < S::WI; ++i) {
-        const uint32_t kb = (uint32_t)opaque((int)keepbits[i]);
+      for (int p = 0; p < PASSES; ++p) {
 #pragma unroll
-        for (int j = 0; j < S::WJ; ++j) {
-          const int m = tok + j * 32;
+        for (int jj = 0; jj < JPP; ++jj) {
+          const int j = p * JPP + jj;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int ch = chb + i * 32 + q * 8;
-            if (m < M && ch < H) st8(ot + (long long)m * H + ch, pack4(acc[i][j], q));
-          }
+          for (int i = 0; i < S::WI; ++i) {
+            RS::put(st, acc[i][j], i, jj * 32, lane);
+            const uint32_t kb = (uint32_t)opaque((int)keepbits[i]);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {  // all ones where register e is a synced channel
-            const uint32_t keep = (uint32_t)((int)(kb << (31 - e)) >> 31);
-            acc[i][j][e] = __uint_as_float(__float_as_uint(acc[i][j][e]) & keep);
+            for (int e = 0; e < 16; ++e) {  // all ones where register e is a synced channel
+              const uint32_t keep = (uint32_t)((int)(kb << (31 - e)) >> 31);
+              acc[i][j][e] = __uint_as_float(__float_as_uint(acc[i][j][e]) & keep);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one block's registers at a time
           }
         }
+        lds_wave_sync();
+        const int tok0 = tkw + p * JPP * 32;
+        RS::drain(st, JPP * 32, lane, [&](int r, int cc, u32x4 v) {
+          const int tok = tok0 + r, ch = chw + cc * 8;
+          if (tok < M && ch < H) st16(ot + (long long)tok * H + ch, v);
+        });
+        lds_wave_sync();
       }
     }
   }
 
-  // Rank T-1: whole groups.  Ranks t < T-1: merge the synced channels into the
-  // groups written at the end of rank t (by this same lane): all of a rank's
-  // groups are read first, then merged and written.
-  for (int u = T - 1; u >= 0; --u) {
-    const int chb = opaque(cl);
-    const int tok = opaque(m0 + wn * S::WN + (lane & 31));
-    uint16_t* ou = out + u * MH;
-    if (u == T - 1) {
+  // End of the tile: the accumulators now hold the synced channels' sums over
+  // all ranks (local channels are zero); they go to the synced positions of
+  // every rank, whose local positions were written at that rank's boundary.
+  __syncthreads();
+  uint16_t* st = smem + wave * (S::WM * S::WN);
 #pragma unroll
-      for (int i = 0; i < S::WI; ++i)
+  for (int i = 0; i < S::WI; ++i)
 #pragma unroll
-        for (int j = 0; j < S::WJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int ch = chb + i * 32 + q * 8, m = tok + j * 32;
-            if (m < M && ch < H) st8(ou + (long long)m * H + ch, pack4(acc[i][j], q));
-          }
-      continue;
+    for (int j = 0; j < S::WJ; ++j) {
+      RS::put(st, acc[i][j], i, j * 32, lane);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    u32x2 old[S::WI][S::WJ][4];
+  lds_wave_sync();
+  // The last boundary's stores cover the same lines: let them complete first.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int rows = min(S::WN, M - tkw);
+  // Mask of this lane's drain chunk (8 channels).  When every chunk of the
+  // wave is all-synced or all-local, synced chunks are written whole;
+  // otherwise each lane takes one channel and writes it where synced.
+  const int ccl = lane % RS::CPR;
+  const int chc = chw + ccl * 8;
+  uint32_t m8 = 0;
+  if (chc < H) {
+    const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + chc);
 #pragma unroll
-    for (int i = 0; i < S::WI; ++i)
+    for (int b = 0; b < 8; ++b) m8 |= (((b < 4 ? mk[0] : mk[1]) >> (8 * (b & 3))) & 0xffu) ? (1u << b) : 0u;
+  }
+  if (!__any(m8 != 0u && m8 != 0xffu)) {
+    RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
+      if (m8 == 0xffu && r < rows) {
+        uint16_t* o = out + (long long)(tkw + r) * H + chw + cc * 8;
+        for (int u = 0; u < T; ++u) st16(o + u * MH, v);
+      }
+    });
+    return;
+  }
 #pragma unroll
-      for (int j = 0; j < S::WJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ch = min(chb + i * 32 + q * 8, H - 4), m = min(tok + j * 32, M - 1);
-          old[i][j][q] = ld8(ou + (long long)m * H + ch);
-        }
-#pragma unroll
-    for (int i = 0; i < S::WI; ++i) {
-      const uint32_t kb = (uint32_t)opaque((int)keepbits[i]);
-#pragma unroll
-      for (int j = 0; j < S::WJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ch = chb + i * 32 + q * 8, m = tok + j * 32;
-          u32x2 sel;  // 0xffff per synced bf16 lane of the group
-          sel[0] = (((kb >> (4 * q)) & 1u) ? 0xffffu : 0u) | (((kb >> (4 * q + 1)) & 1u) ? 0xffff0000u : 0u);
-          sel[1] = (((kb >> (4 * q + 2)) & 1u) ? 0xffffu : 0u) | (((kb >> (4 * q + 3)) & 1u) ? 0xffff0000u : 0u);
-          if (m < M && ch < H && ((kb >> (4 * q)) & 0xfu) != 0u)
-            st8(ou + (long long)m * H + ch, (pack4(acc[i][j], q) & sel) | (old[i][j][q] & ~sel));
-        }
+  for (int h = 0; h < S::WM / 64; ++h) {
+    const int cw = h * 64 + lane;  // channel within the sub-tile
+    const int ch = chw + cw;
+    if (ch < H && mask[ch] != 0) {
+      const uint16_t* sp = st + (cw & 7);
+      uint16_t* o = out + (long long)tkw * H + ch;
+      for (int r = 0; r < rows; ++r) {
+        const uint16_t v = sp[RS::off(r, cw >> 3)];
+        for (int u = 0; u < T; ++u) o[u * MH] = v;
+        o += H;
+      }
     }
   }
 }
@@ -259,27 +277,35 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
       __syncthreads();
     }
     const bool more = c + 1 < nk;
-    if (more) {
-      load_b(c + 1);
-      issue_a(c + 1);
-    }
     mma_chunk<BM, BN>([&](int ks, int i) { return frag_kcont(As, wm * S::WM + i * 32, ks, lane); },
-                      [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc);
+                      [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                      [&] {
+                        if (more) {
+                          load_b(c + 1);
+                          issue_a(c + 1);
+                        }
+                      });
     if (more) store_b(c + 1, smem + ((c + 1) & 1) * S::BUF + BM * kBK);
   }
 
-  uint16_t* dXt = dX + (long long)t * M * Kr;
-  const int kb = k0r + wm * S::WM + (lane >> 5) * 4;
-  const int tok = m0 + wn * S::WN + (lane & 31);
+  // Stage the transposed sub-tile through LDS and write whole rows of dX_t.
+  using RS = RowStage<S::WM>;
+  __syncthreads();
+  uint16_t* st = smem + wave * (S::WM * S::WN);
 #pragma unroll
   for (int i = 0; i < S::WI; ++i)
 #pragma unroll
-    for (int j = 0; j < S::WJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = kb + i * 32 + q * 8, m = tok + j * 32;
-        if (k < Kr && m < M) st8(dXt + (long long)m * Kr + k, pack4(acc[i][j], q));
-      }
+    for (int j = 0; j < S::WJ; ++j) {
+      RS::put(st, acc[i][j], i, j * 32, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  lds_wave_sync();
+  uint16_t* dXt = dX + (long long)t * M * Kr;
+  const int kw = k0r + wm * S::WM, mw = m0 + wn * S::WN;
+  RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
+    const int m = mw + r, k = kw + cc * 8;
+    if (m < M && k < Kr) st16(dXt + (long long)m * Kr + k, v);
+  });
 }
 
 // ============================================================================
@@ -351,27 +377,35 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool more = c + 1 < nk;
-    if (more) {
-      load_a(c + 1);
-      issue_b(c + 1);
-    }
     mma_chunk<BM, BN>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
-                      [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc);
+                      [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                      [&] {
+                        if (more) {
+                          load_a(c + 1);
+                          issue_b(c + 1);
+                        }
+                      });
     if (more) store_a(c + 1, smem + ((c + 1) & 1) * S::BUF);
   }
 
-  uint16_t* dWt = dW + (long long)t * Kr * H;
-  const int cb = c0 + wm * S::WM + (lane >> 5) * 4;
-  const int kr = k0r + wn * S::WN + (lane & 31);
+  // Stage the transposed sub-tile through LDS and write whole rows of dW_t.
+  using RS = RowStage<S::WM>;
+  __syncthreads();
+  uint16_t* st = smem + wave * (S::WM * S::WN);
 #pragma unroll
   for (int i = 0; i < S::WI; ++i)
 #pragma unroll
-    for (int j = 0; j < S::WJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = cb + i * 32 + q * 8, k = kr + j * 32;
-        if (c < H && k < Kr) st8(dWt + (long long)k * H + c, pack4(acc[i][j], q));
-      }
+    for (int j = 0; j < S::WJ; ++j) {
+      RS::put(st, acc[i][j], i, j * 32, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  lds_wave_sync();
+  uint16_t* dWt = dW + (long long)t * Kr * H;
+  const int cw = c0 + wm * S::WM, kw = k0r + wn * S::WN;
+  RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
+    const int k = kw + r, c = cw + cc * 8;
+    if (k < Kr && c < H) st16(dWt + (long long)k * H + c, v);
+  });
 }
 
 }  // namespace caat
