@@ -5,12 +5,13 @@
 //
 //   rowpar_pcr_decode_kernel: one workgroup per (rank t, 64-channel block), so
 //     every weight row piece it reads is one whole 128-byte line.  Its 4 waves
-//     split the contraction; each streams 32-row x 64-channel stages straight
-//     into LDS (buffer loads, 3 stages in flight per wave) and feeds them to
-//     16x16x32 bf16 MFMAs through gfx950's LDS transpose read, with the token
-//     rows of X_t read into A fragments alongside.  The waves' partial sums
-//     are added in wave order through LDS; local channels are written to
-//     out[t] as bf16, synced channels leave their fp32 value in the workspace.
+//     split the contraction; each streams 32-row x 64-channel weight stages
+//     and the matching 32 columns of X_t's token rows straight into LDS
+//     (buffer loads, 3 stages in flight per wave) and feeds them to 16x16x32
+//     bf16 MFMAs, the weights through gfx950's LDS transpose read.  The
+//     waves' partial sums are added in wave order through LDS; local channels
+//     are written to out[t] as bf16, synced channels leave their fp32 value in
+//     the workspace.
 //
 //   decode_sync_sum_kernel: for each synced (token, channel) the T fp32 values
 //     are added in ascending rank order and the one bf16 result is written to
@@ -43,13 +44,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 // swizzled by 2*(k%4) so the 4 k-rows of a transpose read hit distinct banks.
 __device__ __forceinline__ int dec_off(int k, int ch) { return k * kDecCols + (((ch >> 3) ^ ((k & 3) << 1)) << 3) + (ch & 7); }
 
+// X stage layout [32 token rows][32 k], 64-byte rows; 16-byte chunks XOR
+// swizzled by (row / 4) % 4 so the 16 rows of an A-fragment read hit distinct
+// banks.
+__device__ __forceinline__ int dec_xoff(int row, int ch) { return row * kDecStage + ((ch ^ ((row >> 2) & 3)) << 3); }
+
 template <int NB>  // MFMA row blocks of 16 tokens: 1 (M <= 16) or 2
 __global__ void __launch_bounds__(kDecThreads)
 rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                          float* __restrict__ partial, int T, int M, int Kr, int H) {
-  constexpr int SE = kDecStage * kDecCols;  // elements per stage (4 KiB)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kDecWaves * kDecDepth * SE];  // 64 KiB
+  constexpr int SE = kDecStage * kDecCols;   // W elements per stage (4 KiB)
+  constexpr int XE = kDecMaxM * kDecStage;   // X elements per stage (2 KiB)
+  constexpr int SLOT = SE + XE;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kDecWaves * kDecDepth * SLOT];  // 96 KiB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = (H + kDecCols - 1) / kDecCols;
@@ -63,36 +71,30 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int kbeg = min(Kr, wave * kq), kend = min(Kr, kbeg + kq);
   const int nst = (kend - kbeg + kDecStage - 1) / kDecStage;
 
-  // Weight DMA: an instruction moves 8 k-rows x 64 channels (1 KiB); this
-  // lane's slot is k-row lane/8, stored chunk lane%8.  Rows past Kr read as
-  // zero (they only occur past the last wave's end).
+  // Both operands are copied global -> LDS, 4 + NB wave instructions per
+  // stage.  Weight rows past Kr and token rows past M, and X columns past this
+  // wave's range, read as zero (out of the buffer's range).
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + t * KH, (uint32_t)(KH * 2));
   const int wrow = lane >> 3;
   const int wvoff = (wrow * H + (((lane & 7) ^ ((wrow & 3) << 1)) << 3)) * 2;
-  uint16_t* slots = lds + wave * kDecDepth * SE;
-  auto issue_w = [&](int st) {
-    uint16_t* tile = slots + (st % kDecDepth) * SE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int soff = __builtin_amdgcn_readfirstlane(((kbeg + st * kDecStage + 8 * i) * H + n0) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void_t*)(tile + 8 * i * kDecCols), 16, wvoff, soff, 0, 0);
-    }
-  };
-  // A fragments: token row xr (+16 for block 1), k offset xk within the stage.
-  // Rows past M and k past this wave's range are pointed beyond the end of the
-  // X_t buffer, so the load itself returns zeros: every lane always issues the
-  // same loads (the vmcnt accounting below relies on it) and nothing waits on
-  // a select.
-  const int xr = lane & 15, xk = (lane >> 4) * 8;
   const uint32_t xbytes = (uint32_t)(MK * 2);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(Xt, xbytes);
-  auto load_x = [&](int st, u32x4 (&x)[NB]) {
-    const int k = kbeg + st * kDecStage + xk;
+  const int xch = (lane & 3) ^ ((lane >> 4) & 3);  // logical k-chunk this lane copies
+  uint16_t* slots = lds + wave * kDecDepth * SLOT;
+  auto issue = [&](int st) {
+    uint16_t* tile = slots + (st % kDecDepth) * SLOT;
+    const int k0 = kbeg + st * kDecStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int soff = __builtin_amdgcn_readfirstlane(((k0 + 8 * i) * H + n0) * 2);
+      dma16(wrs, tile + 8 * i * kDecCols, wvoff, soff);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int m = xr + 16 * b;
-      const uint32_t voff = (m < M && k < kend) ? (uint32_t)(m * Kr + k) * 2u : xbytes;
-      x[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, voff, 0, 0));
+      const int m = (lane >> 2) + 16 * b;
+      const bool ok = m < M && k0 + xch * 8 < kend;
+      const int voff = ok ? (m * Kr + xch * 8) * 2 : (int)xbytes;
+      dma16(xrs, tile + SE + 16 * b * kDecStage, voff, __builtin_amdgcn_readfirstlane(k0 * 2));
     }
   };
 
@@ -107,48 +109,34 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // tr-read addressing (16x16x32 B operand): lane 4s+u of 16-lane group g
   // names k-row 8g+4h+s and channels 4u..4u+3 of a 16-channel block.
   const int g = lane >> 4, s4 = (lane & 15) >> 2, u4 = lane & 3;
-  auto step = [&](int st, const u32x4 (&xuse)[NB], u32x4 (&xnext)[NB]) {
-    issue_w(st + kDecDepth - 1);  // stages past the end read zeros
-    load_x(st + kDecDepth - 1, xnext);
-    wait_vmcnt<(kDecDepth - 1) * (4 + NB)>();  // stage st has landed
-    const uint16_t* tile = slots + (st % kDecDepth) * SE;
+  auto step = [&](int st) {
+    issue(st + kDecDepth - 1);  // stages past the end read zeros
+    wait_vmcnt<(kDecDepth - 1) * (4 + NB)>();  // this wave's copies of stage st have landed
+    const uint16_t* tile = slots + (st % kDecDepth) * SLOT;
+    u32x4 xa[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xa[b] = ld16(tile + SE + dec_xoff(16 * b + (lane & 15), lane >> 4));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x4 b;
+      u32x4 bv;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = 8 * g + 4 * h + s4;
         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + dec_off(row, j * 16 + 4 * u4)));
         const u32x2 w2 = __builtin_bit_cast(u32x2, v);
-        b[2 * h] = w2[0];
-        b[2 * h + 1] = w2[1];
+        bv[2 * h] = w2[0];
+        bv[2 * h + 1] = w2[1];
       }
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb)
-        acc[bb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xuse[bb]), as_bf16x8(b), acc[bb][j], 0, 0, 0);
+        acc[bb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[bb]), as_bf16x8(bv), acc[bb][j], 0, 0, 0);
     }
     // This slot is refilled by the next step's issue: finish reading it.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // Token fragments for stages st..st+3 rotate through four register sets by
-  // unrolling the stage loop four times (copies would wait on the loads).
-  u32x4 x0[NB], x1[NB], x2[NB], x3[NB];
-  issue_w(0);
-  load_x(0, x0);
-  issue_w(1);
-  load_x(1, x1);
-  issue_w(2);
-  load_x(2, x2);
-  for (int st = 0; st < nst; st += 4) {
-    step(st, x0, x3);
-    if (st + 1 >= nst) break;
-    step(st + 1, x1, x0);
-    if (st + 2 >= nst) break;
-    step(st + 2, x2, x1);
-    if (st + 3 >= nst) break;
-    step(st + 3, x3, x2);
-  }
+  for (int p = 0; p < kDecDepth - 1; ++p) issue(p);
+  for (int st = 0; st < nst; ++st) step(st);
   wait_vmcnt<0>();
   __syncthreads();
 

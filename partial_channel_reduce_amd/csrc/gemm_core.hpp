@@ -15,7 +15,7 @@
 //            ds_read_b64_tr_b16 (gfx950's LDS transpose read: within each
 //            16-lane group, lane 4s+u names 4 consecutive rows of k-row s, and
 //            every lane receives one row's values from the 4 k-rows).
-// Plain operands are copied global -> LDS with global_load_lds_dwordx4 (no
+// Plain operands are copied global -> LDS with buffer_load_dwordx4 ... lds (no
 // register staging); operands that need a per-element select are staged
 // through registers and written with ds_write_b128.
 #pragma once
@@ -47,14 +47,20 @@ using AccTile = f32x16[TileShape<BM, BN>::WI][TileShape<BM, BN>::WJ];
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---- LDS layouts ----------------------------------------------------------------
-// KCONT: element offset of 16-byte chunk `chunk` (0..7) of row `row`.  XOR with
-// row % 8 keeps the 32 rows of an MFMA fragment read on distinct banks.
-__device__ __forceinline__ int kc_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// The LDS serves 256 bytes (64 banks) per cycle, i.e. 16 lanes of a 16-byte
+// read or 32 lanes of an 8-byte read at a time; the swizzles below keep each
+// such group on distinct banks.
+//
+// KCONT: element offset of 16-byte chunk `chunk` (0..7) of row `row`.  Rows are
+// 128 bytes, so a 16-row group spans two rows per bank set; XOR with
+// (row / 2) % 8 gives its 16 rows 16 distinct (row parity, chunk) slots.
+__device__ __forceinline__ int kc_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int kc_off(int row, int chunk) { return row * kBK + ((chunk ^ kc_swz(row)) << 3); }
 // MNCONT with R elements per k-row: element offset of logical chunk `chunk`
-// (0..R/8-1) of k-row `k`.  The swizzle keeps chunk pairs (2c, 2c+1) adjacent
-// and spreads 4 consecutive k-rows over distinct banks.
+// (0..R/8-1) of k-row `k`.  A transpose read by 32 lanes covers 4 k-rows x 4
+// consecutive chunks; XOR with 4 * (k % 4) puts them on 16 distinct chunks.
 template <int R>
-__device__ __forceinline__ int mn_off(int k, int chunk) { return k * R + ((chunk ^ ((k & 3) << 1)) << 3); }
+__device__ __forceinline__ int mn_off(int k, int chunk) { return k * R + ((chunk ^ ((k & 3) << 2)) << 3); }
 
 // ---- direct global -> LDS copies (one wave instruction moves 1 KiB) -------------
 // Buffer loads with an LDS destination.  The per-lane part of the address is
@@ -64,16 +70,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
 
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes from
+// rsrc + voff + soff land at lds + 16 * i.  Written as inline assembly on
+// purpose: the compiler cannot tell which LDS bytes such a copy writes, and
+// if it sees the copy it makes every later LDS read wait until the copy has
+// finished -- which would stall the reads of the current stage behind the
+// loads of the next one.  Users order these copies explicitly: a wait for
+// all of the wave's memory operations, then a workgroup barrier, before the
+// destination is read, and no copy into a buffer that is still being read.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, int voff, int soff) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" : : "s"(la), "v"(voff), "s"(rsrc),
+               "s"(soff));
+}
+
 // KCONT tile: rows r0..r0+R-1 of a row-major [rows][ld] buffer, k0..k0+63.
 // Rows past the buffer read as zero; k past the contraction reads the next
 // row's values, which the caller clears (zero_kcont_tail).
 struct KcDma {
   __amdgpu_buffer_rsrc_t rsrc;
   int voff;  // bytes: this lane's (row in group of 8, swizzled chunk)
-  __device__ __forceinline__ KcDma(const void* base, uint32_t nbytes, int ld, int lane) {
+  // The wave's instructions cover 8-row groups whose index has the wave's
+  // parity, so kc_swz(row) is the same for all of them.
+  __device__ __forceinline__ KcDma(const void* base, uint32_t nbytes, int ld, int lane, int wave) {
     rsrc = make_rsrc(base, nbytes);
     const int r = lane >> 3;
-    voff = (r * ld + (((lane & 7) ^ r) << 3)) * 2;
+    voff = (r * ld + (((lane & 7) ^ kc_swz((wave & 1) * 8 + r)) << 3)) * 2;
   }
   template <int R>
   __device__ __forceinline__ void load(int ld, int r0, int k0, uint16_t* tile, int wave) const {
@@ -81,7 +103,7 @@ struct KcDma {
     for (int i = 0; i < R / 32; ++i) {
       const int rb = (i * 4 + wave) * 8;  // 8 rows per instruction
       const int soff = __builtin_amdgcn_readfirstlane(((r0 + rb) * ld + k0) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + rb * kBK), 16, voff, soff, 0, 0);
+      dma16(rsrc, tile + rb * kBK, voff, soff);
     }
   }
 };
@@ -98,7 +120,7 @@ struct MnDma {
     rsrc = make_rsrc(base, nbytes);
     const int kr = lane / CPR;                 // k-row within the instruction
     const int k = (wave * RPI + kr) & 3;       // (row in tile) % 4, the same for every instruction
-    const int chunk = (lane % CPR) ^ (k << 1);  // logical chunk stored at this lane's slot
+    const int chunk = (lane % CPR) ^ (k << 2);  // logical chunk stored at this lane's slot
     voff = (kr * ld + chunk * 8) * 2;
   }
   __device__ __forceinline__ void load(int ld, int c0, int k0, uint16_t* tile, int wave) const {
@@ -106,7 +128,7 @@ struct MnDma {
     for (int i = 0; i < R / 32; ++i) {
       const int kb = (i * 4 + wave) * RPI;
       const int soff = __builtin_amdgcn_readfirstlane(((k0 + kb) * ld + c0) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + kb * R), 16, voff, soff, 0, 0);
+      dma16(rsrc, tile + kb * R, voff, soff);
     }
   }
 };

@@ -92,7 +92,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
     const int k0 = (c - t * nk) * kBK;
     uint16_t* buf = smem + (c & 1) * S::BUF;
     const MnDma<BM> da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
-    const KcDma db(X + t * MK, (uint32_t)(MK * 2), Kr, lane);
+    const KcDma db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
     da.load(H, c0, k0, buf, wave);
     db.load<BN>(Kr, m0, k0, buf + BM * kBK, wave);
   };
@@ -239,11 +239,10 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
   // Staged B: this thread always owns 16-byte chunk (tid & 7) of its token rows.
   const int my_chunk = tid & 7;
   u32x4 vz[NV], vg[NV];
-  u32x4 sel;
+  u32x2 mk;  // mask bytes of this thread's 8 channels, expanded only when stored
   auto load_b = [&](int c) {
     const int ch = min(c * kBK + my_chunk * 8, H - 8);
-    const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + ch);
-    sel = expand_mask8(mk[0], mk[1]);
+    mk = *reinterpret_cast<const u32x2*>(mask + ch);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int row = min(m0 + ((tid + i * kGemmThreads) >> 3), M - 1);
@@ -255,13 +254,14 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
   auto store_b = [&](int c, uint16_t* Bs) {
     const bool inside = c * kBK + my_chunk * 8 < H;
     const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 sel = expand_mask8(mk[0], mk[1]);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int row = (tid + i * kGemmThreads) >> 3;
       st16(Bs + kc_off(row, my_chunk), inside ? select8(vg[i], vz[i], sel) : z);
     }
   };
-  const KcDma da(Wt, (uint32_t)(KH * 2), H, lane);
+  const KcDma da(Wt, (uint32_t)(KH * 2), H, lane, wave);
   auto issue_a = [&](int c) { da.load<BM>(H, k0r, c * kBK, smem + (c & 1) * S::BUF, wave); };
 
   load_b(0);
