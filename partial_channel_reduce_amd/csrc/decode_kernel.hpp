@@ -28,7 +28,6 @@ constexpr int kDecCols = 64;     // channels per workgroup: one 128-byte line pe
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecStage = 32;    // contraction rows per stage (one MFMA k-step)
-constexpr int kDecDepth = 4;     // stage slots per wave: one being read, three in flight
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -44,7 +43,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // swizzled by 2*(k%4) so the 4 k-rows of a transpose read hit distinct banks.
 __device__ __forceinline__ int dec_off(int k, int ch) { return k * kDecCols + (((ch >> 3) ^ ((k & 3) << 1)) << 3) + (ch & 7); }
 
-// X stage layout [32 token rows][32 k], 64-byte rows; 16-byte chunks XOR
+// X stage layout [16*NB token rows][32 k], 64-byte rows; 16-byte chunks XOR
 // swizzled by (row / 4) % 4 so the 16 rows of an A-fragment read hit distinct
 // banks.
 __device__ __forceinline__ int dec_xoff(int row, int ch) { return row * kDecStage + ((ch ^ ((row >> 2) & 3)) << 3); }
@@ -54,10 +53,16 @@ __global__ void __launch_bounds__(kDecThreads)
 rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                          float* __restrict__ partial, int T, int M, int Kr, int H) {
-  constexpr int SE = kDecStage * kDecCols;   // W elements per stage (4 KiB)
-  constexpr int XE = kDecMaxM * kDecStage;   // X elements per stage (2 KiB)
+  // Stage slots per wave: 4 (3 in flight) with one 16-token block, 3 with two,
+  // so that a workgroup needs at most 80 KiB of LDS and two fit on a CU.
+  constexpr int kDecDepth = NB == 1 ? 4 : 3;
+  constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
+  constexpr int XE = 16 * NB * kDecStage;   // X elements per stage (1 or 2 KiB)
   constexpr int SLOT = SE + XE;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kDecWaves * kDecDepth * SLOT];  // 96 KiB
+  constexpr int LDS = kDecWaves * kDecDepth * SLOT > kDecWaves * kDecMaxM * kDecCols * 2
+                          ? kDecWaves * kDecDepth * SLOT
+                          : kDecWaves * kDecMaxM * kDecCols * 2;  // stages, or the fp32 reduction area
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = (H + kDecCols - 1) / kDecCols;

@@ -70,6 +70,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
 
+// Workgroup barrier for LDS hand-offs: each wave first completes its own LDS
+// accesses; the caller has already waited for whatever copies into LDS the
+// other waves need.  Unlike __syncthreads() it carries no fence, which would
+// also wait for every outstanding global access of the wave (prefetches,
+// stores) although nothing after the barrier depends on them.  The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes from
 // rsrc + voff + soff land at lds + 16 * i.  Written as inline assembly on
 // purpose: the compiler cannot tell which LDS bytes such a copy writes, and

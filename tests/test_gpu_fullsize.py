@@ -46,6 +46,7 @@ def _gather(t, *idx):
     "name,T,M,Kr,H,kind",
     [
         ("Llama2-7B down-proj", 8, 16384, 1376, 4096, "random"),
+        ("Llama2-7B down-proj, S = first half", 8, 16384, 1376, 4096, "prefix"),
         ("Llama2-7B out-proj", 8, 16384, 512, 4096, "random"),
         ("TinyLlama-1.1B down-proj", 8, 32768, 704, 2048, "strided"),
         ("130M down-proj", 8, 8192, 384, 768, "random"),
@@ -72,12 +73,13 @@ def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind):
     _check_sampled_bf16(got, ref, mask[cs] != 0, f"fwd {name}")
 
 
-def test_bwd_7b_full_size_sampled(ops):
+@pytest.mark.parametrize("kind", ["random", "prefix"])
+def test_bwd_7b_full_size_sampled(ops, kind):
     T, M, Kr, H = 8, 16384, 1376, 4096
-    _announce("full-size bwd Llama2-7B down-proj")
+    _announce(f"full-size bwd Llama2-7B down-proj, {kind} mask")
     X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=2)
     dZ = synth.make_grad(T, M, H, seed=2)
-    mask = synth.make_mask(H, 0.5, "random", seed=2)
+    mask = synth.make_mask(H, 0.5, kind, seed=2)
     args = (G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
     dX, dW = ops.pcr_bwd(*args)
     dX2, dW2 = ops.pcr_bwd(*args)
