@@ -160,7 +160,7 @@ def main():
             "rowpar_pcr_fwd_kernel": t_fwd,
             "pcr_bwd_dw_kernel": t_bwd - t_bdx,
             "pcr_bwd_dx_kernel": t_bwd - t_bdw,
-            "grad_sync_sum_kernel": max(t_bdx + t_bdw - t_bwd, 0.0),
+            "pcr_reduce_bf16_kernel (G)": max(t_bdx + t_bdw - t_bwd, 0.0),
         }
         res["kernels_ms"] = {n: round(v, 4) for n, v in k.items()}
         per_flops = {"rowpar_pcr_fwd_kernel": flops_fwd, "pcr_bwd_dw_kernel": flops_fwd, "pcr_bwd_dx_kernel": flops_fwd}

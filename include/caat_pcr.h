@@ -89,8 +89,9 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  *   dX[t] = G_t W_t^T   [M, Kr] bf16      dW[t] = X_t^T G_t   [Kr, H] bf16
  * G's synced channels are rounded to bf16 once (they feed bf16 MFMA); both
  * products accumulate in fp32.  dX or dW may be NULL to skip that product.
- * Needs caat_pcr_bwd_workspace_bytes() bytes of workspace (any contents).
- * Outputs must not overlap the inputs or each other.
+ * Needs caat_pcr_bwd_workspace_bytes() = T*M*H*2 bytes (rounded up to 256)
+ * of workspace, any contents on entry; on return it holds G[T,M,H] (bf16).
+ * Outputs must not overlap the inputs, the workspace or each other.
  */
 int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask,
                  uint16_t* dX, uint16_t* dW, int T, int M, int Kr, int H,

@@ -47,20 +47,34 @@ int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
 }
 
 template <int BM, int BN>
-int launch_dx(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* W, const uint8_t* mask, uint16_t* dX, int T,
-              int M, int Kr, int H, hipStream_t s) {
+int launch_dx(const uint16_t* G, const uint16_t* W, uint16_t* dX, int T, int M, int Kr, int H, hipStream_t s) {
   const int tm = (Kr + BM - 1) / BM, tn = (M + BN - 1) / BN;  // dX column tiles x token tiles
-  hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, dZ, Gs, W, mask, dX,
-                     T, M, Kr, H, tm, tn);
+  hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, G, W, dX, T, M, Kr,
+                     H, tm, tn);
   return launched();
 }
 
 template <int BM, int BN>
-int launch_dw(const uint16_t* dZ, const uint16_t* Gs, const uint16_t* X, const uint8_t* mask, uint16_t* dW, int T,
-              int M, int Kr, int H, hipStream_t s) {
+int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, hipStream_t s) {
   const int tm = (H + BM - 1) / BM, tn = (Kr + BN - 1) / BN;  // channel tiles x dW row tiles
-  hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, dZ, Gs, X, mask, dW,
-                     T, M, Kr, H, tm, tn);
+  hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, G, X, dW, T, M, Kr,
+                     H, tm, tn);
+  return launched();
+}
+
+// bf16 partial channel-reduce of y[T,M,H] into o (o == y: in place).
+int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, hipStream_t s) {
+  const long long mh = (long long)M * H;
+  const uint32_t nvec = (uint32_t)(mh / 8);
+  const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
+  const int ip = (y == o) ? 1 : 0;
+  const uint32_t hv = (uint32_t)(H / 8);
+  switch (T) {
+    case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+    case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+    case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+    default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+  }
   return launched();
 }
 
@@ -128,7 +142,7 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
 
 size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0) return 0;
-  return round256((size_t)M * H * 2);
+  return round256((size_t)T * M * H * 2);  // G_t for every rank, bf16
 }
 
 int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* dX,
@@ -166,19 +180,17 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
     }
     return CAAT_OK;
   }
-  uint16_t* Gs = reinterpret_cast<uint16_t*>(workspace);
-  const uint32_t nvec = (uint32_t)((long long)M * (H / 8));
-  hipLaunchKernelGGL(grad_sync_sum_kernel, dim3((nvec + kReduceThreads - 1) / kReduceThreads), dim3(kReduceThreads),
-                     0, s, dZ, mask, Gs, T, nvec, (uint32_t)(H / 8), (long long)M * H);
-  if (int st = launched()) return st;
+  // G_t = the partial channel-reduce of dZ, for every rank, into the workspace.
+  uint16_t* G = reinterpret_cast<uint16_t*>(workspace);
+  if (int st = launch_reduce_bf16(dZ, mask, G, T, M, H, s)) return st;
   if (dX) {
-    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256>(dZ, Gs, W, mask, dX, T, M, Kr, H, s)
-                                           : launch_dx<128, 128>(dZ, Gs, W, mask, dX, T, M, Kr, H, s);
+    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256>(G, W, dX, T, M, Kr, H, s)
+                                           : launch_dx<128, 128>(G, W, dX, T, M, Kr, H, s);
     if (st) return st;
   }
   if (dW) {
-    const int st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256>(dZ, Gs, X, mask, dW, T, M, Kr, H, s)
-                                           : launch_dw<128, 128>(dZ, Gs, X, mask, dW, T, M, Kr, H, s);
+    const int st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256>(G, X, dW, T, M, Kr, H, s)
+                                           : launch_dw<128, 128>(G, X, dW, T, M, Kr, H, s);
     if (st) return st;
   }
   return CAAT_OK;
@@ -214,18 +226,7 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
       default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
     }
   } else {
-    const uint32_t nvec = (uint32_t)(mh / 8);
-    const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
-    const uint16_t* y = static_cast<const uint16_t*>(Y);
-    uint16_t* o = static_cast<uint16_t*>(out);
-    const int ip = inplace ? 1 : 0;
-    const uint32_t hv = (uint32_t)(H / 8);
-    switch (T) {
-      case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-    }
+    return launch_reduce_bf16(static_cast<const uint16_t*>(Y), mask, static_cast<uint16_t*>(out), T, M, H, s);
   }
   return launched();
 }

@@ -217,20 +217,21 @@ __device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN>& acc
   using S = TileShape<BM, BN>;
   constexpr int NM = S::WI * S::WJ;
   u32x4 a[2][S::WI], b[2][S::WJ];
+  // Fragments are read in the order the MFMAs (i-major) consume them: A0 and
+  // every B first, then the remaining A, so each has most of a k-step to land.
+  auto read = [&](int ks, int p) {
+    a[p][0] = fa(ks, 0);
 #pragma unroll
-  for (int i = 0; i < S::WI; ++i) a[0][i] = fa(0, i);
+    for (int j = 0; j < S::WJ; ++j) b[p][j] = fb(ks, j);
 #pragma unroll
-  for (int j = 0; j < S::WJ; ++j) b[0][j] = fb(0, j);
+    for (int i = 1; i < S::WI; ++i) a[p][i] = fa(ks, i);
+  };
+  read(0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     if (ks == 0) pre();
-    if (ks + 1 < kBK / 16) {
-#pragma unroll
-      for (int i = 0; i < S::WI; ++i) a[(ks + 1) & 1][i] = fa(ks + 1, i);
-#pragma unroll
-      for (int j = 0; j < S::WJ; ++j) b[(ks + 1) & 1][j] = fb(ks + 1, j);
-    }
+    if (ks + 1 < kBK / 16) read(ks + 1, (ks + 1) & 1);
 #pragma unroll
     for (int i = 0; i < S::WI; ++i)
 #pragma unroll

@@ -202,21 +202,21 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   }
 }
 
-// Rank t's reduced gradient, 8 channels: Gs where the mask is set, dZ_t elsewhere.
-__device__ __forceinline__ u32x4 select8(u32x4 gs, u32x4 dz, u32x4 sel) { return (gs & sel) | (dz & ~sel); }
-
 // ============================================================================
-// Backward, input gradient, computed as dX_t^T[k,m] = sum_c W_t[k,c] G_t[m,c].
-// A = W_t (rows k, contraction c contiguous: KCONT, copied directly);
-// B = G_t (rows m: KCONT, staged through registers for the select).
+// Backward.  G_t (the reduced incoming gradient: the sum over ranks on synced
+// channels, rank t's own gradient elsewhere -- the same partial channel-reduce
+// applied to dZ) is materialised beforehand for every rank, so both products
+// read plain operands copied straight into LDS.
+//
+// Input gradient, computed as dX_t^T[k,m] = sum_c W_t[k,c] G_t[m,c]:
+// A = W_t (rows k, contraction over channels c contiguous: KCONT);
+// B = G_t (rows m: KCONT).
 // ============================================================================
 template <int BM, int BN>
 __global__ void __launch_bounds__(kGemmThreads, 1)
-pcr_bwd_dx_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ Gs,
-                  const uint16_t* __restrict__ W, const uint8_t* __restrict__ mask,
-                  uint16_t* __restrict__ dX, int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
+pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W, uint16_t* __restrict__ dX,
+                  int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
   using S = TileShape<BM, BN>;
-  constexpr int NV = BN * 8 / kGemmThreads;  // staged 16-byte vectors per thread
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,64 +228,36 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
   tile_coords(lin - t * per_rank, tiles_m, tiles_n, tm, tn);
   const int k0r = tm * BM, m0 = tn * BN;  // rows of W_t (dX columns), tokens
   const long long MH = (long long)M * H, KH = (long long)Kr * H;
-  const uint16_t* dZt = dZ + t * MH;
-  const uint16_t* Wt = W + t * KH;
   const int nk = (H + kBK - 1) / kBK;
   const int kv_last = H - (nk - 1) * kBK;
 
   f32x16 acc[S::WI][S::WJ];
   zero_acc<BM, BN>(acc);
 
-  // Staged B: this thread always owns 16-byte chunk (tid & 7) of its token rows.
-  const int my_chunk = tid & 7;
-  u32x4 vz[NV], vg[NV];
-  u32x2 mk;  // mask bytes of this thread's 8 channels, expanded only when stored
-  auto load_b = [&](int c) {
-    const int ch = min(c * kBK + my_chunk * 8, H - 8);
-    mk = *reinterpret_cast<const u32x2*>(mask + ch);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int row = min(m0 + ((tid + i * kGemmThreads) >> 3), M - 1);
-      const uint32_t off = (uint32_t)(row * H + ch);
-      vz[i] = ld16(dZt + off);
-      vg[i] = ld16(Gs + off);
-    }
+  const KcDma da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
+  const KcDma db(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
+  auto issue = [&](int c) {
+    uint16_t* buf = smem + (c & 1) * S::BUF;
+    da.load<BM>(H, k0r, c * kBK, buf, wave);
+    db.load<BN>(H, m0, c * kBK, buf + BM * kBK, wave);
   };
-  auto store_b = [&](int c, uint16_t* Bs) {
-    const bool inside = c * kBK + my_chunk * 8 < H;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 sel = expand_mask8(mk[0], mk[1]);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int row = (tid + i * kGemmThreads) >> 3;
-      st16(Bs + kc_off(row, my_chunk), inside ? select8(vg[i], vz[i], sel) : z);
-    }
-  };
-  const KcDma da(Wt, (uint32_t)(KH * 2), H, lane, wave);
-  auto issue_a = [&](int c) { da.load<BM>(H, k0r, c * kBK, smem + (c & 1) * S::BUF, wave); };
 
-  load_b(0);
-  issue_a(0);
-  store_b(0, smem + BM * kBK);
+  issue(0);
   for (int c = 0; c < nk; ++c) {
     uint16_t* As = smem + (c & 1) * S::BUF;
     uint16_t* Bs = As + BM * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (c == nk - 1 && kv_last < kBK) {
+    if (c == nk - 1 && kv_last < kBK) {  // channels past H: the next row's values
       zero_kcont_tail<BM>(As, kv_last, tid);
+      zero_kcont_tail<BN>(Bs, kv_last, tid);
       __syncthreads();
     }
-    const bool more = c + 1 < nk;
     mma_chunk<BM, BN>([&](int ks, int i) { return frag_kcont(As, wm * S::WM + i * 32, ks, lane); },
                       [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                       [&] {
-                        if (more) {
-                          load_b(c + 1);
-                          issue_a(c + 1);
-                        }
+                        if (c + 1 < nk) issue(c + 1);
                       });
-    if (more) store_b(c + 1, smem + ((c + 1) & 1) * S::BUF + BM * kBK);
   }
 
   // Stage the transposed sub-tile through LDS and write whole rows of dX_t.
@@ -309,19 +281,16 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
 }
 
 // ============================================================================
-// Backward, weight gradient, computed as dW_t^T[c,k] = sum_m G_t[m,c] X_t[m,k].
-// The contraction runs over tokens m, the strided index of both operands, so
-// both are MNCONT: A = G_t ([m][c], staged through registers for the select),
-// B = X_t ([m][k], copied directly).
+// Weight gradient, computed as dW_t^T[c,k] = sum_m G_t[m,c] X_t[m,k].  The
+// contraction runs over tokens m, the strided index of both operands, so both
+// are MNCONT: A = G_t ([m][c]), B = X_t ([m][k]).  Token rows past M read as
+// zero (outside the rank's buffer).
 // ============================================================================
 template <int BM, int BN>
 __global__ void __launch_bounds__(kGemmThreads, 1)
-pcr_bwd_dw_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ Gs,
-                  const uint16_t* __restrict__ X, const uint8_t* __restrict__ mask,
-                  uint16_t* __restrict__ dW, int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
+pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X, uint16_t* __restrict__ dW,
+                  int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
   using S = TileShape<BM, BN>;
-  constexpr int CPR = BM / 8;                   // 16-byte chunks per k-row of the A tile
-  constexpr int NV = kBK * CPR / kGemmThreads;  // staged vectors per thread
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -333,59 +302,30 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ 
   tile_coords(lin - t * per_rank, tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, k0r = tn * BN;  // channels (dW columns), rows of dW
   const long long MH = (long long)M * H, MK = (long long)M * Kr;
-  const uint16_t* dZt = dZ + t * MH;
-  const uint16_t* Xt = X + t * MK;
   const int nk = (M + kBK - 1) / kBK;
-  const int kv_last = M - (nk - 1) * kBK;
 
   f32x16 acc[S::WI][S::WJ];
   zero_acc<BM, BN>(acc);
 
-  // Staged A: this thread always owns channel chunk (tid % CPR) of the tile, so
-  // its 8-channel select mask is loaded once.
-  const int my_chunk = tid % CPR;
-  const int ch = min(c0 + my_chunk * 8, H - 8);
-  const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + ch);
-  const u32x4 sel = expand_mask8(mk[0], mk[1]);
-  u32x4 vz[NV], vg[NV];
-  auto load_a = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int m = min(c * kBK + (tid + i * kGemmThreads) / CPR, M - 1);
-      const uint32_t off = (uint32_t)(m * H + ch);
-      vz[i] = ld16(dZt + off);
-      vg[i] = ld16(Gs + off);
-    }
+  const MnDma<BM> da(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
+  const MnDma<BN> db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
+  auto issue = [&](int c) {
+    uint16_t* buf = smem + (c & 1) * S::BUF;
+    da.load(H, c0, c * kBK, buf, wave);
+    db.load(Kr, k0r, c * kBK, buf + BM * kBK, wave);
   };
-  auto store_a = [&](int c, uint16_t* As) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int k = (tid + i * kGemmThreads) / CPR;
-      st16(As + mn_off<BM>(k, my_chunk), c * kBK + k < M ? select8(vg[i], vz[i], sel) : z);
-    }
-  };
-  const MnDma<BN> db(Xt, (uint32_t)(MK * 2), Kr, lane, wave);
-  auto issue_b = [&](int c) { db.load(Kr, k0r, c * kBK, smem + (c & 1) * S::BUF + BM * kBK, wave); };
 
-  load_a(0);
-  issue_b(0);
-  store_a(0, smem);
+  issue(0);
   for (int c = 0; c < nk; ++c) {
     uint16_t* As = smem + (c & 1) * S::BUF;
     uint16_t* Bs = As + BM * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool more = c + 1 < nk;
     mma_chunk<BM, BN>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
                       [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                       [&] {
-                        if (more) {
-                          load_a(c + 1);
-                          issue_b(c + 1);
-                        }
+                        if (c + 1 < nk) issue(c + 1);
                       });
-    if (more) store_a(c + 1, smem + ((c + 1) & 1) * S::BUF);
   }
 
   // Stage the transposed sub-tile through LDS and write whole rows of dW_t.

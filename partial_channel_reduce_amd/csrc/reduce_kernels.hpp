@@ -1,6 +1,6 @@
 // HBM-streaming kernels of the partial channel-reduce:
-//   * the standalone reduce over per-rank activations Y[T,M,H] (fp32 or bf16);
-//   * the backward's sync-set gradient Gs[m,c] = sum_t dZ[t,m,c] for c in S.
+//   * the standalone reduce over per-rank activations Y[T,M,H] (fp32 or bf16),
+//     which in bf16 also forms the backward's reduced gradient G from dZ.
 //
 // Definition (CAAT-Net paper, Introduction): only the hidden channels of the
 // sync set S are summed over the T tensor-parallel ranks; the other channels
@@ -156,32 +156,6 @@ pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint
         if ((sel[e >> 1] >> (16 * (e & 1))) & 1u) o[e] = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
     }
   }
-}
-
-// ---- backward: Gs[m, c] = bf16( sum_t dZ[t, m, c] ) for c in S ---------------
-// Gs is [M, H] bf16; vectors with no synced channel are skipped (never read by
-// the GEMM loaders, which select Gs only where the mask is set).
-__global__ void __launch_bounds__(kReduceThreads)
-grad_sync_sum_kernel(const uint16_t* __restrict__ dZ, const uint8_t* __restrict__ mask,
-                     uint16_t* __restrict__ Gs, int T, uint32_t nvec, uint32_t hvec, long long mh) {
-  const uint32_t v = blockIdx.x * kReduceThreads + threadIdx.x;
-  if (v >= nvec) return;
-  const int c = (int)(v % hvec) * 8;
-  const long long base = (long long)v * 8;
-  const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
-  if ((mk[0] | mk[1]) == 0u) return;
-  float s[8];
-  bf16x8_to_f32(ld16(dZ + base), s);
-  for (int t = 1; t < T; ++t) {
-    float f[8];
-    bf16x8_to_f32(ld16(dZ + t * mh + base), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += f[e];
-  }
-  u32x4 sv;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
-  st16(Gs + base, sv);
 }
 
 // Small fill kernel (used instead of a runtime memset so the call sequence can

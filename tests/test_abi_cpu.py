@@ -105,7 +105,7 @@ def test_workspace_sizes(L):
     for M in (1, 8, 32):
         need = L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H)
         assert need >= T * M * H * 4 and need % 256 == 0
-    assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) >= 16384 * H * 2
+    assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) >= T * 16384 * H * 2  # G for every rank
     assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) % 256 == 0
     assert L.caat_pcr_bwd_workspace_bytes(T, 0, Kr, H) == 0
     assert L.caat_pcr_bwd_workspace_bytes(0, 8, Kr, H) == 0  # invalid dims report 0
