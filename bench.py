@@ -242,7 +242,7 @@ def main():
         for Md in DEC_M:
             Xs = [randn_bf16((T, Md, KR)) for _ in range(nsets)]
             outs = [torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
-            wsd = torch.empty(max(1, ops.fwd_workspace_bytes(T, Md, KR, H)), dtype=torch.uint8, device=dev)
+            wsd = torch.zeros(max(1, ops.fwd_workspace_bytes(T, Md, KR, H)), dtype=torch.uint8, device=dev)
             idx = [0]
 
             def call():

@@ -103,9 +103,16 @@ const char* caat_status_string(int status) {
   }
 }
 
+// Decode-shaped calls: a few tokens, and one rank's fp32 partials [M][H]
+// addressable with 32-bit byte offsets.
+static bool use_decode(int M, int H) { return M > 0 && M <= kDecMaxM && (size_t)M * H * 4 < ((size_t)1 << 31); }
+
+// Arrival counters of the decode kernel: one int per 64-channel block.
+static size_t decode_counter_bytes(int H) { return round256((size_t)((H + kDecCols - 1) / kDecCols) * sizeof(int)); }
+
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
-  if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0 || M > kDecMaxM) return 0;
-  return round256((size_t)T * M * H * sizeof(float));
+  if (check_dims(T, M, Kr, H) != CAAT_OK || !use_decode(M, H)) return 0;
+  return decode_counter_bytes(H) + round256((size_t)T * M * H * sizeof(float));
 }
 
 int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M,
@@ -125,15 +132,17 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
   }
   if (M == 0) return CAAT_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (M <= kDecMaxM) {
-    float* partial = static_cast<float*>(workspace);
+  if (use_decode(M, H)) {
+    // workspace: the per-block arrival counters, then the fp32 partials
+    int* arrivals = static_cast<int*>(workspace);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(H));
     const dim3 grid(((H + kDecCols - 1) / kDecCols) * T);
     if (M <= 16)
-      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, T, M, Kr, H);
+      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, arrivals,
+                         T, M, Kr, H);
     else
-      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<2>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, T, M, Kr, H);
-    if (int st = launched()) return st;
-    hipLaunchKernelGGL(decode_sync_sum_kernel, dim3((M * H + 255) / 256), dim3(256), 0, s, partial, mask, out, T, M, H);
+      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<2>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, arrivals,
+                         T, M, Kr, H);
     return launched();
   }
   if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256>(X, W, mask, out, T, M, Kr, H, s);

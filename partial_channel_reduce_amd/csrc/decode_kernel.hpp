@@ -1,22 +1,21 @@
 // Decode-shaped forward (M <= 32 tokens): the same result as the fused
 // forward, organised for weight streaming.  With so few tokens the layer reads
 // ~T*Kr*H*2 bytes of weights once and does almost no arithmetic per byte, so
-// it runs as two kernels laid out for HBM streaming:
+// it runs as one kernel laid out for HBM streaming:
 //
 //   rowpar_pcr_decode_kernel: one workgroup per (rank t, 64-channel block), so
 //     every weight row piece it reads is one whole 128-byte line.  Its 4 waves
-//     split the contraction; each streams 32-row x 64-channel weight stages
-//     and the matching 32 columns of X_t's token rows straight into LDS
-//     (buffer loads, 3 stages in flight per wave) and feeds them to 16x16x32
-//     bf16 MFMAs, the weights through gfx950's LDS transpose read.  The
-//     waves' partial sums are added in wave order through LDS; local channels
-//     are written to out[t] as bf16, synced channels leave their fp32 value in
-//     the workspace.
-//
-//   decode_sync_sum_kernel: for each synced (token, channel) the T fp32 values
-//     are added in ascending rank order and the one bf16 result is written to
-//     every rank.  The kernel boundary orders it after the first kernel; no
-//     atomics or device-wide fences are involved.
+//     split the contraction; each keeps three 32-row x 64-channel weight
+//     stages (and the matching 32 columns of X_t's token rows) loading into
+//     registers, and writes each stage through its own small LDS slot into
+//     16x16x32 bf16 MFMAs, the weights via gfx950's LDS transpose read.
+//     (Plain loads into registers stream faster here than copies straight
+//     into LDS.)  The waves' partial sums are added in wave order through
+//     LDS; local channels are written to out[t] as bf16, synced channels
+//     leave their fp32 value in the workspace.  The last of the T workgroups
+//     of a channel block to finish (an arrival counter per block, in the
+//     workspace) adds the synced values in ascending rank order and writes
+//     the one bf16 result to every rank.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -52,16 +51,15 @@ template <int NB>  // MFMA row blocks of 16 tokens: 1 (M <= 16) or 2
 __global__ void __launch_bounds__(kDecThreads)
 rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
-                         float* __restrict__ partial, int T, int M, int Kr, int H) {
-  // Stage slots per wave: 4 (3 in flight) with one 16-token block, 3 with two,
-  // so that a workgroup needs at most 80 KiB of LDS and two fit on a CU.
-  constexpr int kDecDepth = NB == 1 ? 4 : 3;
+                         float* __restrict__ partial, int* __restrict__ arrivals, int T, int M, int Kr,
+                         int H) {
+  constexpr int D = 4;                      // stages held in registers: one being used, three loading
   constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
   constexpr int XE = 16 * NB * kDecStage;   // X elements per stage (1 or 2 KiB)
-  constexpr int SLOT = SE + XE;
-  constexpr int LDS = kDecWaves * kDecDepth * SLOT > kDecWaves * kDecMaxM * kDecCols * 2
-                          ? kDecWaves * kDecDepth * SLOT
-                          : kDecWaves * kDecMaxM * kDecCols * 2;  // stages, or the fp32 reduction area
+  constexpr int SLOT = SE + XE;             // one LDS slot per wave
+  constexpr int LDS = kDecWaves * SLOT > kDecWaves * kDecMaxM * kDecCols * 2
+                          ? kDecWaves * SLOT
+                          : kDecWaves * kDecMaxM * kDecCols * 2;  // slots, or the fp32 reduction area
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -69,39 +67,49 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int t = blockIdx.x / nb;
   const int n0 = (blockIdx.x - t * nb) * kDecCols;
   const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
-  const uint16_t* Xt = X + t * MK;
 
   // This wave's share of the contraction: a multiple of 32 rows per wave.
   const int kq = (((Kr + kDecWaves - 1) / kDecWaves) + kDecStage - 1) / kDecStage * kDecStage;
   const int kbeg = min(Kr, wave * kq), kend = min(Kr, kbeg + kq);
   const int nst = (kend - kbeg + kDecStage - 1) / kDecStage;
 
-  // Both operands are copied global -> LDS, 4 + NB wave instructions per
-  // stage.  Weight rows past Kr and token rows past M, and X columns past this
-  // wave's range, read as zero (out of the buffer's range).
+  // Operands are loaded into registers D-1 stages ahead (plain buffer loads:
+  // the compiler tracks them and waits exactly), then written to this wave's
+  // LDS slot for the transposing reads.  Per lane and stage: 4 weight pieces
+  // (k-row lane/8 + 8i, 16-byte chunk lane%8) and NB token pieces (token row
+  // lane/4 + 16b, k-chunk lane%4).  Weight rows past Kr, token rows past M and
+  // X columns past this wave's range read as zero (out of the buffer's range).
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + t * KH, (uint32_t)(KH * 2));
-  const int wrow = lane >> 3;
-  const int wvoff = (wrow * H + (((lane & 7) ^ ((wrow & 3) << 1)) << 3)) * 2;
   const uint32_t xbytes = (uint32_t)(MK * 2);
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(Xt, xbytes);
-  const int xch = (lane & 3) ^ ((lane >> 4) & 3);  // logical k-chunk this lane copies
-  uint16_t* slots = lds + wave * kDecDepth * SLOT;
-  auto issue = [&](int st) {
-    uint16_t* tile = slots + (st % kDecDepth) * SLOT;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X + t * MK, xbytes);
+  const int wr = lane >> 3, wc = lane & 7;
+  const int wvoff = (wr * H + wc * 8) * 2;
+  const int xr = lane >> 2, xc = lane & 3;
+  struct Stage {
+    u32x4 w[4];
+    u32x4 x[NB];
+  };
+  // Stages past this wave's last one are loaded too, wholly out of range (no
+  // memory traffic, zeros): every load is unconditional, which lets the
+  // compiler count outstanding loads exactly across the unrolled loop.
+  const int wend = (int)(KH * 2);
+  auto load = [&](int st, Stage& S) {
+    const bool live = st < nst;
     const int k0 = kbeg + st * kDecStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int soff = __builtin_amdgcn_readfirstlane(((k0 + 8 * i) * H + n0) * 2);
-      dma16(wrs, tile + 8 * i * kDecCols, wvoff, soff);
-    }
+    for (int i = 0; i < 4; ++i)
+      S.w[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     wrs, wvoff, __builtin_amdgcn_readfirstlane(live ? ((k0 + 8 * i) * H + n0) * 2 : wend), 0));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int m = (lane >> 2) + 16 * b;
-      const bool ok = m < M && k0 + xch * 8 < kend;
-      const int voff = ok ? (m * Kr + xch * 8) * 2 : (int)xbytes;
-      dma16(xrs, tile + SE + 16 * b * kDecStage, voff, __builtin_amdgcn_readfirstlane(k0 * 2));
+      const int m = xr + 16 * b;
+      const bool ok = live && m < M && k0 + xc * 8 < kend;
+      const int voff = ok ? (m * Kr + k0 + xc * 8) * 2 : (int)xbytes;
+      S.x[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, voff, 0, 0));
     }
   };
+  uint16_t* slot = lds + wave * SLOT;
 
   f32x4_t acc[NB][4];
 #pragma unroll
@@ -114,20 +122,22 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // tr-read addressing (16x16x32 B operand): lane 4s+u of 16-lane group g
   // names k-row 8g+4h+s and channels 4u..4u+3 of a 16-channel block.
   const int g = lane >> 4, s4 = (lane & 15) >> 2, u4 = lane & 3;
-  auto step = [&](int st) {
-    issue(st + kDecDepth - 1);  // stages past the end read zeros
-    wait_vmcnt<(kDecDepth - 1) * (4 + NB)>();  // this wave's copies of stage st have landed
-    const uint16_t* tile = slots + (st % kDecDepth) * SLOT;
+  auto use = [&](const Stage& S) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st16(slot + dec_off(wr + 8 * i, wc * 8), S.w[i]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) st16(slot + SE + dec_xoff(xr + 16 * b, xc), S.x[b]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes land before its reads
     u32x4 xa[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xa[b] = ld16(tile + SE + dec_xoff(16 * b + (lane & 15), lane >> 4));
+    for (int b = 0; b < NB; ++b) xa[b] = ld16(slot + SE + dec_xoff(16 * b + (lane & 15), lane >> 4));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 bv;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = 8 * g + 4 * h + s4;
-        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + dec_off(row, j * 16 + 4 * u4)));
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(slot + dec_off(row, j * 16 + 4 * u4)));
         const u32x2 w2 = __builtin_bit_cast(u32x2, v);
         bv[2 * h] = w2[0];
         bv[2 * h + 1] = w2[1];
@@ -136,13 +146,23 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
       for (int bb = 0; bb < NB; ++bb)
         acc[bb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[bb]), as_bf16x8(bv), acc[bb][j], 0, 0, 0);
     }
-    // This slot is refilled by the next step's issue: finish reading it.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the slot is rewritten
   };
 
-  for (int p = 0; p < kDecDepth - 1; ++p) issue(p);
-  for (int st = 0; st < nst; ++st) step(st);
-  wait_vmcnt<0>();
+  // Stage st lives in register set st % D; the loop is unrolled D times so
+  // every set is named statically (a copy would wait on its loads).  The
+  // stage count is padded up to a multiple of D with all-zero stages, so the
+  // loop has no early exits.
+  Stage r[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) load(j, r[j]);
+  for (int st = 0; st < nst; st += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      load(st + j + D - 1, r[(j + D - 1) % D]);
+      use(r[j]);
+    }
+  }
   __syncthreads();
 
   // Add the waves' partial products in wave order.  Accumulator layout
@@ -156,34 +176,70 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
       for (int e = 0; e < 4; ++e)
         red[(wave * kDecMaxM + 16 * b + 4 * g + e) * kDecCols + 16 * j + (lane & 15)] = acc[b][j][e];
   __syncthreads();
-  const int cl = tid % kDecCols, c = n0 + cl;
-  if (c >= H) return;
-  const bool synced = mask[c] != 0;
-  for (int m = tid / kDecCols; m < M; m += kDecThreads / kDecCols) {
-    float y = red[(0 * kDecMaxM + m) * kDecCols + cl];
+  // Each thread takes 4 adjacent channels (16 bytes of fp32) of token rows
+  // tid/16, tid/16 + 16, ...
+  const int q = tid & 15, c4 = n0 + 4 * q;
+  const bool inb = c4 < H;  // H is a multiple of 8, so all 4 channels are in range
+  const uint32_t mbits = inb ? *reinterpret_cast<const uint32_t*>(mask + c4) : 0u;
+  bool syn[4];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) y += red[(w * kDecMaxM + m) * kDecCols + cl];
-    const long long off = t * MH + (long long)m * H + c;
-    if (synced)
-      partial[off] = y;
-    else
-      out[off] = f32_to_bf16(y);
+  for (int e = 0; e < 4; ++e) syn[e] = ((mbits >> (8 * e)) & 0xffu) != 0;
+  const bool any_syn = syn[0] | syn[1] | syn[2] | syn[3];
+  // fp32 partials of rank t, [M][H]: written and read with device-scope
+  // coherent (sc1) 16-byte accesses.
+  constexpr int kSc1 = 1 << 4;
+  const __amdgpu_buffer_rsrc_t prs_t = make_rsrc(partial + t * MH, (uint32_t)(MH * 4));
+  if (inb) {
+    for (int m = tid >> 4; m < M; m += kDecThreads / 16) {
+      f32x4_t y = *reinterpret_cast<const f32x4_t*>(red + (0 * kDecMaxM + m) * kDecCols + 4 * q);
+#pragma unroll
+      for (int w = 1; w < kDecWaves; ++w) y += *reinterpret_cast<const f32x4_t*>(red + (w * kDecMaxM + m) * kDecCols + 4 * q);
+      const long long off = t * MH + (long long)m * H + c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!syn[e]) out[off + e] = f32_to_bf16(y[e]);
+      if (any_syn)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), prs_t, (m * H + c4) * 4, 0, kSc1);
+    }
   }
-}
 
-// Synced channels: out[t][m][c] = bf16( sum_t partial[t][m][c] ), ascending t.
-__global__ void __launch_bounds__(256)
-decode_sync_sum_kernel(const float* __restrict__ partial, const uint8_t* __restrict__ mask,
-                       uint16_t* __restrict__ out, int T, int M, int H) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * H) return;
-  const int c = i % H;
-  if (mask[c] == 0) return;
-  const long long MH = (long long)M * H;
-  float s = partial[i];
-  for (int t = 1; t < T; ++t) s += partial[t * MH + i];
-  const uint16_t v = f32_to_bf16(s);
-  for (int t = 0; t < T; ++t) out[t * MH + i] = v;
+  // The T workgroups of one channel block (one per rank) each publish their
+  // synced fp32 values, then count themselves in; the last to arrive adds
+  // the T values in ascending rank order, writes the one bf16 result to every
+  // rank and returns the counter to zero for the next call.  The partials
+  // and the counter use device-scope coherent accesses, which need no cache
+  // write-back or invalidation across the chip's L2 slices: waiting for the
+  // stores' acknowledgement before the arrival is counted orders them.
+  __shared__ int is_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int blk = blockIdx.x - t * nb;
+  if (tid == 0) is_last = __hip_atomic_fetch_add(arrivals + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == T - 1;
+  __syncthreads();
+  if (!is_last) return;
+  if (tid == 0) __hip_atomic_store(arrivals + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!any_syn) return;
+  for (int m = tid >> 4; m < M; m += kDecThreads / 16) {
+    const int voff = (m * H + c4) * 4;
+    f32x4_t y;
+    for (int u0 = 0; u0 < T; u0 += 8) {  // 8 ranks' loads in flight, then added in rank order
+      f32x4_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (u0 + k < T)
+          v[k] = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(partial + (u0 + k) * MH, (uint32_t)(MH * 4)), voff, 0, kSc1));
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (u0 + k < T) y = (u0 + k == 0) ? v[k] : y + v[k];
+    }
+    for (int u = 0; u < T; ++u) {
+      const long long off = u * MH + (long long)m * H + c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (syn[e]) out[off + e] = f32_to_bf16(y[e]);
+    }
+  }
 }
 
 }  // namespace caat

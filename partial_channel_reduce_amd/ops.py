@@ -115,7 +115,10 @@ def bwd_workspace_bytes(T: int, M: int, Kr: int, H: int) -> int:
 
 def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """out[T,M,H] = partial channel-reduce of X[t] @ W[t] (see caat_pcr.h)."""
+    """out[T,M,H] = partial channel-reduce of X[t] @ W[t] (see caat_pcr.h).
+
+    A caller-supplied `workspace` for decode-shaped calls (M <= 32) must be
+    zeroed once before its first use; the library leaves its counters zero."""
     _require(X, "X", torch.bfloat16, 3)
     dev = X.device
     _require(W, "W", torch.bfloat16, 3, dev)
@@ -131,7 +134,8 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
         raise ValueError(f"out must be {(T, M, H)}, got {tuple(out.shape)}")
     need = fwd_workspace_bytes(T, M, Kr, H)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        # the decode kernel's arrival counters at its head must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().caat_rowpar_pcr_fwd(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, _ptr(workspace), ws_bytes,
                                    _stream(dev))

@@ -223,6 +223,25 @@ def test_decode_repeated_calls(ops):
         assert np.array_equal(got, oracle.rowpar_pcr_fwd(X, W, mask))
 
 
+def test_decode_shared_workspace(ops):
+    """One workspace serves back-to-back decode calls of different sizes: the
+    per-block arrival counters at its head are zero again after every call,
+    and the partials region may hold anything on entry."""
+    T, Kr, H = 8, 512, 1032
+    ws = torch.zeros(ops.fwd_workspace_bytes(T, 32, Kr, H), dtype=torch.uint8, device=G.dev())
+    nblk = (H + 63) // 64
+    cnt_bytes = (nblk * 4 + 255) // 256 * 256  # one int per 64-channel block, padded to 256 bytes
+    ws[cnt_bytes:].fill_(0x7F)  # partials: arbitrary bytes
+    for i, M in enumerate((32, 8, 1, 32, 17)):
+        _announce(f"decode shared workspace call {i} M={M}")
+        X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=20 + i, lo=-1, hi=1, x_zero_frac=0.5)
+        mask = synth.make_mask(H, 0.5, "random", seed=20 + i)
+        out = ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(G.from_dev_bf16(out), oracle.rowpar_pcr_fwd(X, W, mask))
+        assert int(ws[:cnt_bytes].count_nonzero()) == 0, "arrival counters not returned to zero"
+
+
 # ---------------------------------------------------------------------------
 # backward
 # ---------------------------------------------------------------------------
