@@ -93,6 +93,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // memory traffic, zeros): every load is unconditional, which lets the
   // compiler count outstanding loads exactly across the unrolled loop.
   const int wend = (int)(KH * 2);
+  constexpr int kNt = 1 << 1;  // weights are read once: non-temporal (streaming) loads
   auto load = [&](int st, Stage& S) {
     const bool live = st < nst;
     const int k0 = kbeg + st * kDecStage;
@@ -100,7 +101,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
     for (int i = 0; i < 4; ++i)
       S.w[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     wrs, wvoff, __builtin_amdgcn_readfirstlane(live ? ((k0 + 8 * i) * H + n0) * 2 : wend), 0));
+                     wrs, wvoff, __builtin_amdgcn_readfirstlane(live ? ((k0 + 8 * i) * H + n0) * 2 : wend), kNt));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int m = xr + 16 * b;
