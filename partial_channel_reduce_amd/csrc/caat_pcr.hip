@@ -62,6 +62,13 @@ int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, 
   return launched();
 }
 
+// Second argument of the reduce kernels: half the grid when the workgroup
+// order is to alternate between the two halves of the rows (even grid, rank
+// slices a multiple of 16 MiB apart), else 0.
+static uint32_t reduce_half(const dim3& grid, long long slice_bytes) {
+  return (grid.x % 2 == 0 && slice_bytes % (16ll << 20) == 0) ? grid.x / 2 : 0u;
+}
+
 // bf16 partial channel-reduce of y[T,M,H] into o (o == y: in place).
 int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, hipStream_t s) {
   const long long mh = (long long)M * H;
@@ -69,11 +76,12 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
   const int ip = (y == o) ? 1 : 0;
   const uint32_t hv = (uint32_t)(H / 8);
+  const uint32_t hf = reduce_half(grid, mh * 2);
   switch (T) {
-    case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-    case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-    case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-    default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+    case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+    case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+    case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+    default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
   }
   return launched();
 }
@@ -227,12 +235,13 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
     float* o = static_cast<float*>(out);
     const int ip = inplace ? 1 : 0;
     const uint32_t hv = (uint32_t)(H / 4);
+    const uint32_t hf = reduce_half(grid, mh * 4);
     switch (T) {
-      case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      case 4: hipLaunchKernelGGL(pcr_reduce_f32_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      case 8: hipLaunchKernelGGL(pcr_reduce_f32_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
-      default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip); break;
+      case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+      case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+      case 4: hipLaunchKernelGGL(pcr_reduce_f32_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+      case 8: hipLaunchKernelGGL(pcr_reduce_f32_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+      default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
     }
   } else {
     return launch_reduce_bf16(static_cast<const uint16_t*>(Y), mask, static_cast<uint16_t*>(out), T, M, H, s);

