@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,out,reduce,decode,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
@@ -91,15 +91,15 @@ def main():
     ops.lib()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    legs = set(args.only.split(",")) if args.only else {"train", "out", "reduce", "decode"}
+    legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
     def randn_bf16(shape, scale=1.0):
         return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * scale).to(torch.bfloat16)
 
-    def mask_dev(Hh, seed=0):
-        return torch.from_numpy(synth.make_mask(Hh, P, "random", seed=seed)).to(dev)
+    def mask_dev(Hh, seed=0, kind="random"):
+        return torch.from_numpy(synth.make_mask(Hh, P, kind, seed=seed)).to(dev)
 
     def time_call(fn, iters, warm=2):
         for _ in range(warm):
@@ -178,6 +178,33 @@ def main():
         }
         res["fwd_tflops"] = round(flops_fwd / (t_fwd * 1e-3) / 1e12, 2)
         res["bwd_tflops"] = round(2 * flops_fwd / (t_bwd * 1e-3) / 1e12, 2)
+
+    if "train" in legs and "context" in legs:
+        # The same step with S = the first half of the channels.  A contiguous
+        # S (reachable for any S by one model-wide channel permutation) lets
+        # the forward write the synced sums as whole lines.
+        mkp = mask_dev(H, kind="prefix")
+        t_pf = time_call(lambda: ops.rowpar_pcr_fwd(X, W, mkp, out=out), it)
+        t_pb = time_call(lambda: ops.pcr_bwd(dZ, X, W, mkp, dX=dX, dW=dW, workspace=ws), it)
+        res["prefix_mask"] = {"fwd_ms": round(t_pf, 4), "bwd_ms": round(t_pb, 4),
+                              "tflops": round(flops_step / ((t_pf + t_pb) * 1e-3) / 1e12, 2)}
+
+        # Context only (not part of the path): the vendor GEMM library
+        # (hipBLASLt through torch.bmm) on the three plain per-rank products of
+        # the same shapes, without any reduce.  Both operands contiguous.
+        yb = torch.empty((T, M, H), dtype=torch.bfloat16, device=dev)
+        wt = W.transpose(1, 2).contiguous()
+        xt = X.transpose(1, 2).contiguous()
+        t_lf = time_call(lambda: torch.bmm(X, W, out=yb), it)
+        t_lx = time_call(lambda: torch.bmm(dZ, wt, out=dX), it)
+        t_lw = time_call(lambda: torch.bmm(xt, dZ, out=dW), it)
+        res["library_gemm"] = {
+            "what": "torch.bmm (hipBLASLt), plain products of the same shapes, no reduce",
+            "fwd_ms": round(t_lf, 4), "dx_ms": round(t_lx, 4), "dw_ms": round(t_lw, 4),
+            "tflops": round(flops_step / ((t_lf + t_lx + t_lw) * 1e-3) / 1e12, 2),
+        }
+        del yb, wt, xt
+    if "train" in legs:
         del X, W, dZ, out, dX, dW, ws
         torch.cuda.empty_cache()
 
@@ -303,6 +330,8 @@ def main():
         "kernels_ms": res.get("kernels_ms"),
         "fwd_tflops": res.get("fwd_tflops"),
         "bwd_tflops": res.get("bwd_tflops"),
+        "prefix_mask": res.get("prefix_mask"),
+        "library_gemm": res.get("library_gemm"),
         "out_proj": res.get("out_proj"),
         "reduce_only_f32": res.get("reduce_only_f32"),
         "decode_down_proj": res.get("decode_down_proj"),
