@@ -425,7 +425,7 @@ def rocprof_traffic_summary(fetch_dir: str, write_dir: str) -> str:
         rb, wb = fetch[k] * sf * 1024, write[k] * sw * 1024
         out.append(f"| {_short(k)} | {nf[k]} | {fetch[k]:.0f} | {write[k]:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
         base = _short(k).split("<")[0]
-        if base.startswith(("rowpar_pcr", "pcr_bwd", "grad_sync", "pcr_reduce", "decode_sync")):
+        if base.startswith(("rowpar_pcr", "pcr_bwd", "pcr_reduce")):
             lines.append(f"`traffic {base} src={cur} bytes={int(rb + wb)} read={int(rb)} write={int(wb)}`")
     return "\n".join(out + ["", "Machine-readable (kernel, kernel-source hash, calibrated bytes per dispatch):", ""]
                      + [ln + "  " for ln in lines])

@@ -38,30 +38,6 @@ __device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// LDS tiles hold operands as [row][64 k] bf16 rows of 128 bytes, i.e. eight
-// 16-byte k-chunks per row.  The chunk index is XOR-swizzled with a function of
-// the row so that (a) the MFMA operand reads (32 consecutive rows, one chunk)
-// and (b) the transposing writes (rows 8 apart, one chunk) both spread over
-// all 32 banks.
-__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {  // in bf16 elements
-  return row * 64 + ((chunk ^ lds_swz(row)) << 3);
-}
-
-// 8x8 bf16 transpose held in registers: r[i] holds 8 consecutive columns of
-// row i; on return o[j] holds column j as 8 consecutive rows.
-__device__ __forceinline__ void transpose8x8(const u32x4 r[8], u32x4 o[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t a = r[2 * d][j >> 1];
-      const uint32_t b = r[2 * d + 1][j >> 1];
-      o[j][d] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-}
-
 // Block-id remap for 8-XCD parts: consecutive hardware block ids land on
 // different XCDs (round robin), so hand each XCD a contiguous range of logical
 // tiles; tiles that share operand rows then share that XCD's L2.

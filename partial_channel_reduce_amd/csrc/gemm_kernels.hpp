@@ -40,7 +40,10 @@ __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcn
 // A = W_t^T (channels x k, W is [k][c]: MNCONT); B = X_t (tokens x k: KCONT).
 // All stores are staged through LDS so that they write whole lines: at a
 // rank boundary through the LDS buffer of the chunk just consumed (the next
-// chunk is landing in the other one), at the end through all of LDS.
+// chunk is landing in the other one), at the end through all of LDS.  They
+// are non-temporal: the output is never re-read here, and streaming it past
+// the caches keeps the operands' lines (and the end-of-tile partial-line
+// writes) from contending with it (measured: 4-6% faster).
 // ============================================================================
 template <int BM, int BN>
 __global__ void __launch_bounds__(kGemmThreads, 1)
@@ -143,7 +146,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
         const int tok0 = tkw + p * JPP * 32;
         RS::drain(st, JPP * 32, lane, [&](int r, int cc, u32x4 v) {
           const int tok = tok0 + r, ch = chw + cc * 8;
-          if (tok < M && ch < H) st16(ot + (long long)tok * H + ch, v);
+          if (tok < M && ch < H) st16_nt(ot + (long long)tok * H + ch, v);
         });
         lds_wave_sync();
       }
@@ -181,7 +184,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
     RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
       if (m8 == 0xffu && r < rows) {
         uint16_t* o = out + (long long)(tkw + r) * H + chw + cc * 8;
-        for (int u = 0; u < T; ++u) st16(o + u * MH, v);
+        for (int u = 0; u < T; ++u) st16_nt(o + u * MH, v);
       }
     });
     return;
@@ -195,7 +198,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
       uint16_t* o = out + (long long)tkw * H + ch;
       for (int r = 0; r < rows; ++r) {
         const uint16_t v = sp[RS::off(r, cw >> 3)];
-        for (int u = 0; u < T; ++u) o[u * MH] = v;
+        for (int u = 0; u < T; ++u) __builtin_nontemporal_store(v, o + u * MH);
         o += H;
       }
     }
