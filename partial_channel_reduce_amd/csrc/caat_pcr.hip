@@ -37,27 +37,32 @@ int launched() { return hipGetLastError() == hipSuccess ? CAAT_OK : CAAT_ERR_LAU
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-template <int BM, int BN>
+// Waves per workgroup of the 256x256-tile GEMMs: eight (two per SIMD, each
+// with a 128x64 sub-tile) hide LDS and barrier waits behind the other wave's
+// MFMAs; the 128x128 tiles of small problems keep four.
+constexpr int kBigTileWaves = 8;
+
+template <int BM, int BN, int NW>
 int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
                int H, hipStream_t s) {
   const int tm = (H + BM - 1) / BM, tn = (M + BN - 1) / BN;  // channel tiles x token tiles
-  hipLaunchKernelGGL((rowpar_pcr_fwd_kernel<BM, BN>), dim3(tm * tn), dim3(kGemmThreads), 0, s, X, W, mask, out, T,
+  hipLaunchKernelGGL((rowpar_pcr_fwd_kernel<BM, BN, NW>), dim3(tm * tn), dim3(NW * 64), 0, s, X, W, mask, out, T,
                      M, Kr, H, tm, tn);
   return launched();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 int launch_dx(const uint16_t* G, const uint16_t* W, uint16_t* dX, int T, int M, int Kr, int H, hipStream_t s) {
   const int tm = (Kr + BM - 1) / BM, tn = (M + BN - 1) / BN;  // dX column tiles x token tiles
-  hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, G, W, dX, T, M, Kr,
+  hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN, NW>), dim3(T * tm * tn), dim3(NW * 64), 0, s, G, W, dX, T, M, Kr,
                      H, tm, tn);
   return launched();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, hipStream_t s) {
   const int tm = (H + BM - 1) / BM, tn = (Kr + BN - 1) / BN;  // channel tiles x dW row tiles
-  hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN>), dim3(T * tm * tn), dim3(kGemmThreads), 0, s, G, X, dW, T, M, Kr,
+  hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN, NW>), dim3(T * tm * tn), dim3(NW * 64), 0, s, G, X, dW, T, M, Kr,
                      H, tm, tn);
   return launched();
 }
@@ -153,8 +158,8 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
                          T, M, Kr, H);
     return launched();
   }
-  if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256>(X, W, mask, out, T, M, Kr, H, s);
-  return launch_fwd<128, 128>(X, W, mask, out, T, M, Kr, H, s);
+  if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s);
+  return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
 }
 
 size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H) {
@@ -201,13 +206,13 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
   uint16_t* G = reinterpret_cast<uint16_t*>(workspace);
   if (int st = launch_reduce_bf16(dZ, mask, G, T, M, H, s)) return st;
   if (dX) {
-    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256>(G, W, dX, T, M, Kr, H, s)
-                                           : launch_dx<128, 128>(G, W, dX, T, M, Kr, H, s);
+    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256, kBigTileWaves>(G, W, dX, T, M, Kr, H, s)
+                                           : launch_dx<128, 128, 4>(G, W, dX, T, M, Kr, H, s);
     if (st) return st;
   }
   if (dW) {
-    const int st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256>(G, X, dW, T, M, Kr, H, s)
-                                           : launch_dw<128, 128>(G, X, dW, T, M, Kr, H, s);
+    const int st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256, kBigTileWaves>(G, X, dW, T, M, Kr, H, s)
+                                           : launch_dw<128, 128, 4>(G, X, dW, T, M, Kr, H, s);
     if (st) return st;
   }
   return CAAT_OK;

@@ -1,9 +1,10 @@
 // bf16 MFMA GEMM building blocks for gfx950 (CDNA4).
 //
-// A workgroup of 256 threads (4 wave64s in a 2x2 grid) owns a BM x BN output
-// tile and walks the contraction in 64-wide chunks, double buffered in LDS.
-// Each wave accumulates its (BM/2) x (BN/2) sub-tile with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).
+// A workgroup of NW wave64s (a 2 x NW/2 grid) owns a BM x BN output tile and
+// walks the contraction in 64-wide chunks, double buffered in LDS.  Each wave
+// accumulates its (BM/2) x (2*BN/NW) sub-tile with v_mfma_f32_32x32x16_bf16
+// (fp32 accumulation).  With NW = 8 two waves share each SIMD, so one wave's
+// LDS and barrier waits are covered by the other's MFMAs.
 //
 // Operands are described by where their contraction index k is contiguous in
 // global memory, and each kind keeps that orientation in LDS:
@@ -24,25 +25,27 @@
 
 namespace caat {
 
-constexpr int kGemmThreads = 256;
 constexpr int kBK = 64;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-template <int BM, int BN>
+template <int BM, int BN, int NW = 4>
 struct TileShape {
-  static constexpr int WM = BM / 2, WN = BN / 2;    // per-wave sub-tile (2x2 waves)
+  static constexpr int THREADS = NW * 64;
+  static constexpr int WGN = NW / 2;                // waves along BN (2 along BM)
+  static constexpr int WM = BM / 2, WN = BN / WGN;  // per-wave sub-tile
   static constexpr int WI = WM / 32, WJ = WN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int BUF = (BM + BN) * kBK;       // one stage, bf16 elements
   static constexpr int LDS_ELEMS = 2 * BUF;         // double buffer
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must be a multiple of 64");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && WN % 32 == 0, "tile must be a multiple of 64");
 };
 
 // Accumulators of one wave: WI x WJ blocks of 32x32 fp32.
-template <int BM, int BN>
-using AccTile = f32x16[TileShape<BM, BN>::WI][TileShape<BM, BN>::WJ];
+template <int BM, int BN, int NW>
+using AccTile = f32x16[TileShape<BM, BN, NW>::WI][TileShape<BM, BN, NW>::WJ];
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -105,11 +108,11 @@ struct KcDma {
     const int r = lane >> 3;
     voff = (r * ld + (((lane & 7) ^ kc_swz((wave & 1) * 8 + r)) << 3)) * 2;
   }
-  template <int R>
+  template <int R, int NW>
   __device__ __forceinline__ void load(int ld, int r0, int k0, uint16_t* tile, int wave) const {
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      const int rb = (i * 4 + wave) * 8;  // 8 rows per instruction
+    for (int i = 0; i < R / (8 * NW); ++i) {
+      const int rb = (i * NW + wave) * 8;  // 8 rows per instruction
       const int soff = __builtin_amdgcn_readfirstlane(((r0 + rb) * ld + k0) * 2);
       dma16(rsrc, tile + rb * kBK, voff, soff);
     }
@@ -131,10 +134,11 @@ struct MnDma {
     const int chunk = (lane % CPR) ^ (k << 2);  // logical chunk stored at this lane's slot
     voff = (kr * ld + chunk * 8) * 2;
   }
+  template <int NW>
   __device__ __forceinline__ void load(int ld, int c0, int k0, uint16_t* tile, int wave) const {
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      const int kb = (i * 4 + wave) * RPI;
+    for (int i = 0; i < R / (8 * NW); ++i) {
+      const int kb = (i * NW + wave) * RPI;
       const int soff = __builtin_amdgcn_readfirstlane(((k0 + kb) * ld + c0) * 2);
       dma16(rsrc, tile + kb * R, voff, soff);
     }
@@ -144,11 +148,11 @@ struct MnDma {
 // Zero the part of a staged KCONT chunk that lies beyond the contraction
 // (k >= kvalid within the chunk).  Called after the chunk has landed and
 // before it is read.
-template <int R>
+template <int R, int NTHREADS>
 __device__ __forceinline__ void zero_kcont_tail(uint16_t* tile, int kvalid, int tid) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   const int c0 = kvalid >> 3;  // first 16-byte chunk to clear (kvalid % 8 == 0)
-  for (int q = tid; q < R * 8; q += kGemmThreads) {
+  for (int q = tid; q < R * 8; q += NTHREADS) {
     const int row = q >> 3, c = q & 7;
     if (c >= c0) st16(tile + kc_off(row, c), z);
   }
@@ -196,12 +200,12 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
   tn = in / gsz;
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void zero_acc(AccTile<BM, BN>& acc) {
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void zero_acc(AccTile<BM, BN, NW>& acc) {
 #pragma unroll
-  for (int i = 0; i < TileShape<BM, BN>::WI; ++i)
+  for (int i = 0; i < TileShape<BM, BN, NW>::WI; ++i)
 #pragma unroll
-    for (int j = 0; j < TileShape<BM, BN>::WJ; ++j)
+    for (int j = 0; j < TileShape<BM, BN, NW>::WJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
@@ -212,9 +216,9 @@ __device__ __forceinline__ void zero_acc(AccTile<BM, BN>& acc) {
 // global load, so neither the LDS nor the load queue issues in a burst that
 // would leave the matrix core idle.
 // fa(ks, i) / fb(ks, j) return the A / B fragments of block i / j.
-template <int BM, int BN, class FA, class FB, class PRE>
-__device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN>& acc, PRE&& pre) {
-  using S = TileShape<BM, BN>;
+template <int BM, int BN, int NW, class FA, class FB, class PRE>
+__device__ __forceinline__ void mma_chunk(FA&& fa, FB&& fb, AccTile<BM, BN, NW>& acc, PRE&& pre) {
+  using S = TileShape<BM, BN, NW>;
   constexpr int NM = S::WI * S::WJ;
   u32x4 a[2][S::WI], b[2][S::WJ];
   // Fragments are read in the order the MFMAs (i-major) consume them: A0 and

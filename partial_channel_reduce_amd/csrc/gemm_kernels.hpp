@@ -45,22 +45,22 @@ __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcn
 // the caches keeps the operands' lines (and the end-of-tile partial-line
 // writes) from contending with it (measured: 4-6% faster).
 // ============================================================================
-template <int BM, int BN>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+template <int BM, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
 rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                       const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                       int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
-  using S = TileShape<BM, BN>;
+  using S = TileShape<BM, BN, NW>;
   using RS = RowStage<S::WM>;
-  constexpr int REG = S::BUF / 4;              // boundary staging per wave (elements)
+  constexpr int REG = S::BUF / NW;             // boundary staging per wave (elements)
   constexpr int PASSES = S::WM * S::WN / REG;  // boundary passes over the wave's sub-tile
   constexpr int JPP = S::WJ / PASSES;          // 32-token blocks per pass
   static_assert(PASSES * REG == S::WM * S::WN && JPP * PASSES == S::WJ, "staging split");
-  static_assert(4 * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
+  static_assert(NW * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, m0 = tn * BN;  // channel tile, token tile
@@ -88,7 +88,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   }
 
   f32x16 acc[S::WI][S::WJ];
-  zero_acc<BM, BN>(acc);
+  zero_acc<BM, BN, NW>(acc);
 
   auto issue = [&](int c) {
     const int t = c / nk;
@@ -96,8 +96,8 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
     uint16_t* buf = smem + (c & 1) * S::BUF;
     const MnDma<BM> da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
     const KcDma db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
-    da.load(H, c0, k0, buf, wave);
-    db.load<BN>(Kr, m0, k0, buf + BM * kBK, wave);
+    da.template load<NW>(H, c0, k0, buf, wave);
+    db.load<BN, NW>(Kr, m0, k0, buf + BM * kBK, wave);
   };
 
   issue(0);
@@ -109,10 +109,10 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kc == nk - 1 && kv_last < kBK) {  // W's rows past Kr arrived as zeros
-        zero_kcont_tail<BN>(Bs, kv_last, tid);
+        zero_kcont_tail<BN, S::THREADS>(Bs, kv_last, tid);
         __syncthreads();
       }
-      mma_chunk<BM, BN>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
+      mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
                         [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                         [&] {
                           if (c + 1 < nchunks) issue(c + 1);
@@ -215,15 +215,15 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 // A = W_t (rows k, contraction over channels c contiguous: KCONT);
 // B = G_t (rows m: KCONT).
 // ============================================================================
-template <int BM, int BN>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+template <int BM, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
 pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W, uint16_t* __restrict__ dX,
                   int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
-  using S = TileShape<BM, BN>;
+  using S = TileShape<BM, BN, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int per_rank = tiles_m * tiles_n;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int t = lin / per_rank;
@@ -235,14 +235,14 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W
   const int kv_last = H - (nk - 1) * kBK;
 
   f32x16 acc[S::WI][S::WJ];
-  zero_acc<BM, BN>(acc);
+  zero_acc<BM, BN, NW>(acc);
 
   const KcDma da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
   const KcDma db(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
   auto issue = [&](int c) {
     uint16_t* buf = smem + (c & 1) * S::BUF;
-    da.load<BM>(H, k0r, c * kBK, buf, wave);
-    db.load<BN>(H, m0, c * kBK, buf + BM * kBK, wave);
+    da.load<BM, NW>(H, k0r, c * kBK, buf, wave);
+    db.load<BN, NW>(H, m0, c * kBK, buf + BM * kBK, wave);
   };
 
   issue(0);
@@ -252,11 +252,11 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (c == nk - 1 && kv_last < kBK) {  // channels past H: the next row's values
-      zero_kcont_tail<BM>(As, kv_last, tid);
-      zero_kcont_tail<BN>(Bs, kv_last, tid);
+      zero_kcont_tail<BM, S::THREADS>(As, kv_last, tid);
+      zero_kcont_tail<BN, S::THREADS>(Bs, kv_last, tid);
       __syncthreads();
     }
-    mma_chunk<BM, BN>([&](int ks, int i) { return frag_kcont(As, wm * S::WM + i * 32, ks, lane); },
+    mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_kcont(As, wm * S::WM + i * 32, ks, lane); },
                       [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                       [&] {
                         if (c + 1 < nk) issue(c + 1);
@@ -289,15 +289,15 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W
 // are MNCONT: A = G_t ([m][c]), B = X_t ([m][k]).  Token rows past M read as
 // zero (outside the rank's buffer).
 // ============================================================================
-template <int BM, int BN>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+template <int BM, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
 pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X, uint16_t* __restrict__ dW,
                   int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
-  using S = TileShape<BM, BN>;
+  using S = TileShape<BM, BN, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int per_rank = tiles_m * tiles_n;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int t = lin / per_rank;
@@ -308,14 +308,14 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
   const int nk = (M + kBK - 1) / kBK;
 
   f32x16 acc[S::WI][S::WJ];
-  zero_acc<BM, BN>(acc);
+  zero_acc<BM, BN, NW>(acc);
 
   const MnDma<BM> da(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
   const MnDma<BN> db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
   auto issue = [&](int c) {
     uint16_t* buf = smem + (c & 1) * S::BUF;
-    da.load(H, c0, c * kBK, buf, wave);
-    db.load(Kr, k0r, c * kBK, buf + BM * kBK, wave);
+    da.template load<NW>(H, c0, c * kBK, buf, wave);
+    db.template load<NW>(Kr, k0r, c * kBK, buf + BM * kBK, wave);
   };
 
   issue(0);
@@ -324,7 +324,7 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
     uint16_t* Bs = As + BM * kBK;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    mma_chunk<BM, BN>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
+    mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
                       [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                       [&] {
                         if (c + 1 < nk) issue(c + 1);
