@@ -34,13 +34,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 template <int BM, int BN, int NW = 4>
 struct TileShape {
   static constexpr int THREADS = NW * 64;
-  static constexpr int WGN = NW / 2;                // waves along BN (2 along BM)
-  static constexpr int WM = BM / 2, WN = BN / WGN;  // per-wave sub-tile
+  static constexpr int WGM = 2, WGN = NW / 2;       // waves along BM, BN
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave sub-tile
   static constexpr int WI = WM / 32, WJ = WN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int BUF = (BM + BN) * kBK;       // one stage, bf16 elements
   static constexpr int LDS_ELEMS = 2 * BUF;         // double buffer
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && WN % 32 == 0, "tile must be a multiple of 64");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && WM % 32 == 0 && WN % 32 == 0, "tile must be a multiple of 64");
 };
 
 // Accumulators of one wave: WI x WJ blocks of 32x32 fp32.
