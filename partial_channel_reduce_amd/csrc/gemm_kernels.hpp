@@ -33,10 +33,10 @@ __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcn
 // of all T ranks in rank order.  Synced channels keep accumulating across the
 // rank boundaries, so their fp32 accumulator ends as the sum over ranks
 // (ascending t), formed once and written to every rank: bit-identical synced
-// channels.  At the end of rank t the tile is written to out[t] (its synced
-// positions hold a partial sum there and are overwritten at the end) and the
-// local accumulators restart from zero.  At the end the synced channels are
-// written to every rank.
+// channels.  At the end of rank t < T-1 the tile is written to out[t] (its
+// synced positions hold a partial sum there and are overwritten at the end)
+// and the local accumulators restart from zero.  At the end the last rank's
+// tile is written whole and the synced channels go to every other rank.
 // A = W_t^T (channels x k, W is [k][c]: MNCONT); B = X_t (tokens x k: KCONT).
 // All stores are staged through LDS so that they write whole lines: at a
 // rank boundary through the LDS buffer of the chunk just consumed (the next
@@ -118,10 +118,10 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
                           if (c + 1 < nchunks) issue(c + 1);
                         });
     }
-    {
-      // End of rank t: stage and write the tile to out[t], restart the local
-      // channels.  The staging area is this wave's quarter of the buffer the
-      // last chunk was read from.
+    if (t < T - 1) {
+      // End of rank t < T-1: stage and write the tile to out[t], restart the
+      // local channels.  The staging area is this wave's share of the buffer
+      // the last chunk was read from.
       __syncthreads();
       uint16_t* st = smem + ((c - 1) & 1) * S::BUF + wave * REG;
       uint16_t* ot = out + t * MH;
@@ -154,8 +154,9 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   }
 
   // End of the tile: the accumulators now hold the synced channels' sums over
-  // all ranks (local channels are zero); they go to the synced positions of
-  // every rank, whose local positions were written at that rank's boundary.
+  // all ranks and the last rank's local channels, i.e. the last rank's output,
+  // which is written whole; the synced sums then go to the synced positions
+  // of every other rank, whose local positions were written at its boundary.
   __syncthreads();
   uint16_t* st = smem + wave * (S::WM * S::WN);
 #pragma unroll
@@ -166,8 +167,17 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
       __builtin_amdgcn_sched_barrier(0);
     }
   lds_wave_sync();
-  // The last boundary's stores cover the same lines: let them complete first.
+  // The earlier boundaries' stores cover lines written below: let them
+  // complete first.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  {
+    uint16_t* ol = out + (T - 1) * MH;
+    RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
+      const int tok = tkw + r, ch = chw + cc * 8;
+      if (tok < M && ch < H) st16_nt(ol + (long long)tok * H + ch, v);
+    });
+  }
+  if (T == 1) return;
   const int rows = min(S::WN, M - tkw);
   // Mask of this lane's drain chunk (8 channels).  When every chunk of the
   // wave is all-synced or all-local, synced chunks are written whole;
@@ -184,7 +194,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
     RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
       if (m8 == 0xffu && r < rows) {
         uint16_t* o = out + (long long)(tkw + r) * H + chw + cc * 8;
-        for (int u = 0; u < T; ++u) st16_nt(o + u * MH, v);
+        for (int u = 0; u < T - 1; ++u) st16_nt(o + u * MH, v);
       }
     });
     return;
@@ -198,7 +208,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
       uint16_t* o = out + (long long)tkw * H + ch;
       for (int r = 0; r < rows; ++r) {
         const uint16_t v = sp[RS::off(r, cw >> 3)];
-        for (int u = 0; u < T; ++u) __builtin_nontemporal_store(v, o + u * MH);
+        for (int u = 0; u < T - 1; ++u) __builtin_nontemporal_store(v, o + u * MH);
         o += H;
       }
     }
