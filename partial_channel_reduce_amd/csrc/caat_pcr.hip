@@ -67,11 +67,12 @@ int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, 
   return launched();
 }
 
-// Second argument of the reduce kernels: half the grid when the workgroup
-// order is to alternate between the two halves of the rows (even grid, rank
-// slices a multiple of 16 MiB apart), else 0.
-static uint32_t reduce_half(const dim3& grid, long long slice_bytes) {
-  return (grid.x % 2 == 0 && slice_bytes % (16ll << 20) == 0) ? grid.x / 2 : 0u;
+// Last argument of the reduce kernels: how many row regions consecutive
+// workgroups alternate between -- 8 when the rank slices are a multiple of
+// 256 MiB apart, 2 when a multiple of 16 MiB, else 1 (the grid must divide).
+static uint32_t reduce_groups(const dim3& grid, long long slice_bytes) {
+  const uint32_t g = slice_bytes % (256ll << 20) == 0 ? 8u : slice_bytes % (16ll << 20) == 0 ? 2u : 1u;
+  return grid.x % g == 0 ? g : 1u;
 }
 
 // bf16 partial channel-reduce of y[T,M,H] into o (o == y: in place).
@@ -81,7 +82,7 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
   const int ip = (y == o) ? 1 : 0;
   const uint32_t hv = (uint32_t)(H / 8);
-  const uint32_t hf = reduce_half(grid, mh * 2);
+  const uint32_t hf = reduce_groups(grid, mh * 2);
   switch (T) {
     case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
     case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
@@ -240,7 +241,7 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
     float* o = static_cast<float*>(out);
     const int ip = inplace ? 1 : 0;
     const uint32_t hv = (uint32_t)(H / 4);
-    const uint32_t hf = reduce_half(grid, mh * 4);
+    const uint32_t hf = reduce_groups(grid, mh * 4);
     switch (T) {
       case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
       case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
