@@ -5,12 +5,13 @@
 //
 //   rowpar_pcr_decode_kernel: one workgroup per (rank t, 64-channel block), so
 //     every weight row piece it reads is one whole 128-byte line.  Its 4 waves
-//     split the contraction; each keeps three 32-row x 64-channel weight
-//     stages (and the matching 32 columns of X_t's token rows) loading into
-//     registers, and writes each stage through its own small LDS slot into
-//     16x16x32 bf16 MFMAs, the weights via gfx950's LDS transpose read.
-//     (Plain loads into registers stream faster here than copies straight
-//     into LDS.)  The waves' partial sums are added in wave order through
+//     split the contraction (interleaved 32-row stages); each keeps three
+//     32-row x 64-channel weight stages (and the matching 32 columns of X_t's
+//     token rows) loading into registers, and writes each stage through its
+//     own small LDS slot into 16x16x32 bf16 MFMAs, the weights via gfx950's
+//     LDS transpose read.  (Plain loads into registers stream faster here
+//     than copies straight into LDS; with the MFMAs removed the kernel is no
+//     faster: it is bound by the weight stream.)  The waves' partial sums are added in wave order through
 //     LDS; local channels are written to out[t] as bf16, synced channels
 //     leave their fp32 value in the workspace.  The last of the T workgroups
 //     of a channel block to finish (an arrival counter per block, in the
@@ -68,17 +69,17 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int n0 = (blockIdx.x - t * nb) * kDecCols;
   const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
 
-  // This wave's share of the contraction: a multiple of 32 rows per wave.
-  const int kq = (((Kr + kDecWaves - 1) / kDecWaves) + kDecStage - 1) / kDecStage * kDecStage;
-  const int kbeg = min(Kr, wave * kq), kend = min(Kr, kbeg + kq);
-  const int nst = (kend - kbeg + kDecStage - 1) / kDecStage;
+  // This wave's share of the contraction: 32-row stages wave, wave + 4,
+  // wave + 8, ... (the workgroup's waves read adjacent row groups together).
+  const int ns_all = (Kr + kDecStage - 1) / kDecStage;
+  const int nst = (ns_all - wave + kDecWaves - 1) / kDecWaves;
 
   // Operands are loaded into registers D-1 stages ahead (plain buffer loads:
   // the compiler tracks them and waits exactly), then written to this wave's
   // LDS slot for the transposing reads.  Per lane and stage: 4 weight pieces
   // (k-row lane/8 + 8i, 16-byte chunk lane%8) and NB token pieces (token row
   // lane/4 + 16b, k-chunk lane%4).  Weight rows past Kr, token rows past M and
-  // X columns past this wave's range read as zero (out of the buffer's range).
+  // X columns past Kr read as zero (out of the buffer's range).
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + t * KH, (uint32_t)(KH * 2));
   const uint32_t xbytes = (uint32_t)(MK * 2);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X + t * MK, xbytes);
@@ -96,7 +97,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   constexpr int kNt = 1 << 1;  // weights are read once: non-temporal (streaming) loads
   auto load = [&](int st, Stage& S) {
     const bool live = st < nst;
-    const int k0 = kbeg + st * kDecStage;
+    const int k0 = (st * kDecWaves + wave) * kDecStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       S.w[i] = __builtin_bit_cast(
@@ -105,7 +106,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int m = xr + 16 * b;
-      const bool ok = live && m < M && k0 + xc * 8 < kend;
+      const bool ok = live && m < M && k0 + xc * 8 < Kr;
       const int voff = ok ? (m * Kr + k0 + xc * 8) * 2 : (int)xbytes;
       S.x[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, voff, 0, 0));
     }
