@@ -5,7 +5,7 @@
 //
 //   rowpar_pcr_decode_kernel: one workgroup per (rank t, 64-channel block), so
 //     every weight row piece it reads is one whole 128-byte line.  Its 4 waves
-//     split the contraction (interleaved 32-row stages); each keeps three
+//     split the contraction (interleaved 32-row stages); each keeps two
 //     32-row x 64-channel weight stages (and the matching 32 columns of X_t's
 //     token rows) loading into registers, and writes each stage through its
 //     own small LDS slot into 16x16x32 bf16 MFMAs, the weights via gfx950's
@@ -54,7 +54,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                          float* __restrict__ partial, int* __restrict__ arrivals, int T, int M, int Kr,
                          int H) {
-  constexpr int D = 4;                      // stages held in registers: one being used, three loading
+  constexpr int D = 3;                      // stages held in registers: one being used, two loading
   constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
   constexpr int XE = 16 * NB * kDecStage;   // X elements per stage (1 or 2 KiB)
   constexpr int SLOT = SE + XE;             // one LDS slot per wave
