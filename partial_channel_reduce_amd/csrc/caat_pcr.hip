@@ -121,7 +121,7 @@ const char* caat_status_string(int status) {
 // addressable with 32-bit byte offsets.
 static bool use_decode(int M, int H) { return M > 0 && M <= kDecMaxM && (size_t)M * H * 4 < ((size_t)1 << 31); }
 
-// Arrival counters of the decode kernel: one int per 64-channel block.
+// Arrival counters of the decode kernel: one int per channel block.
 static size_t decode_counter_bytes(int H) { return round256((size_t)((H + kDecCols - 1) / kDecCols) * sizeof(int)); }
 
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {

@@ -3,10 +3,10 @@
 // ~T*Kr*H*2 bytes of weights once and does almost no arithmetic per byte, so
 // it runs as one kernel laid out for HBM streaming:
 //
-//   rowpar_pcr_decode_kernel: one workgroup per (rank t, 64-channel block), so
-//     every weight row piece it reads is one whole 128-byte line.  Its 4 waves
+//   rowpar_pcr_decode_kernel: one workgroup per (rank t, 128-channel block),
+//     so every weight row piece it reads is 256 contiguous bytes.  Its 8 waves
 //     split the contraction (interleaved 32-row stages); each keeps two
-//     32-row x 64-channel weight stages (and the matching 32 columns of X_t's
+//     32-row x 128-channel weight stages (and the matching 32 columns of X_t's
 //     token rows) loading into registers, and writes each stage through its
 //     own small LDS slot into 16x16x32 bf16 MFMAs, the weights via gfx950's
 //     LDS transpose read.  (Plain loads into registers stream faster here
@@ -24,10 +24,13 @@
 namespace caat {
 
 constexpr int kDecMaxM = 32;     // two 16-row MFMA blocks
-constexpr int kDecCols = 64;     // channels per workgroup: one 128-byte line per row
-constexpr int kDecWaves = 4;
+constexpr int kDecCols = 128;    // channels per workgroup: 256 bytes of each weight row
+constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecStage = 32;    // contraction rows per stage (one MFMA k-step)
+constexpr int kDecLpr = kDecCols / 8;       // lanes per weight row piece (16 bytes each)
+constexpr int kDecRpi = 64 / kDecLpr;       // weight rows per load instruction
+constexpr int kDecLoads = kDecStage / kDecRpi;  // weight loads per stage
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -39,9 +42,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// LDS stage layout [32 k][64 channels], 128-byte rows; 16-byte chunks XOR
-// swizzled by 2*(k%4) so the 4 k-rows of a transpose read hit distinct banks.
-__device__ __forceinline__ int dec_off(int k, int ch) { return k * kDecCols + (((ch >> 3) ^ ((k & 3) << 1)) << 3) + (ch & 7); }
+// LDS stage layout [32 k][128 channels], 256-byte rows (one pass over the 64
+// banks each); 16-byte chunks XOR swizzled by 2*(k%4) + 8*((k/8)%2): a
+// transpose read serves 32 lanes at a time, k-rows {k..k+3} and {k+8..k+11}
+// of two 16-channel pieces, which this spreads over all 64 banks.
+__device__ __forceinline__ int dec_off(int k, int ch) {
+  return k * kDecCols + (((ch >> 3) ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 3) + (ch & 7);
+}
 
 // X stage layout [16*NB token rows][32 k], 64-byte rows; 16-byte chunks XOR
 // swizzled by (row / 4) % 4 so the 16 rows of an A-fragment read hit distinct
@@ -54,13 +61,14 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                          float* __restrict__ partial, int* __restrict__ arrivals, int T, int M, int Kr,
                          int H) {
-  constexpr int D = 3;                      // stages held in registers: one being used, two loading
+  constexpr int D = 2;                      // stages held in registers: one being used, one loading
   constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
   constexpr int XE = 16 * NB * kDecStage;   // X elements per stage (1 or 2 KiB)
   constexpr int SLOT = SE + XE;             // one LDS slot per wave
-  constexpr int LDS = kDecWaves * SLOT > kDecWaves * kDecMaxM * kDecCols * 2
+  constexpr int RR = 16 * NB;               // token rows of the fp32 reduction area
+  constexpr int LDS = kDecWaves * SLOT > kDecWaves * RR * kDecCols * 2
                           ? kDecWaves * SLOT
-                          : kDecWaves * kDecMaxM * kDecCols * 2;  // slots, or the fp32 reduction area
+                          : kDecWaves * RR * kDecCols * 2;  // slots, or the fp32 reduction area
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -76,18 +84,18 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
 
   // Operands are loaded into registers D-1 stages ahead (plain buffer loads:
   // the compiler tracks them and waits exactly), then written to this wave's
-  // LDS slot for the transposing reads.  Per lane and stage: 4 weight pieces
-  // (k-row lane/8 + 8i, 16-byte chunk lane%8) and NB token pieces (token row
+  // LDS slot for the transposing reads.  Per lane and stage: 8 weight pieces
+  // (k-row lane/16 + 4i, 16-byte chunk lane%16) and NB token pieces (token row
   // lane/4 + 16b, k-chunk lane%4).  Weight rows past Kr, token rows past M and
   // X columns past Kr read as zero (out of the buffer's range).
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + t * KH, (uint32_t)(KH * 2));
   const uint32_t xbytes = (uint32_t)(MK * 2);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X + t * MK, xbytes);
-  const int wr = lane >> 3, wc = lane & 7;
+  const int wr = lane / kDecLpr, wc = lane % kDecLpr;
   const int wvoff = (wr * H + wc * 8) * 2;
   const int xr = lane >> 2, xc = lane & 3;
   struct Stage {
-    u32x4 w[4];
+    u32x4 w[kDecLoads];
     u32x4 x[NB];
   };
   // Stages past this wave's last one are loaded too, wholly out of range (no
@@ -99,10 +107,10 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
     const bool live = st < nst;
     const int k0 = (st * kDecWaves + wave) * kDecStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kDecLoads; ++i)
       S.w[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     wrs, wvoff, __builtin_amdgcn_readfirstlane(live ? ((k0 + 8 * i) * H + n0) * 2 : wend), kNt));
+                     wrs, wvoff, __builtin_amdgcn_readfirstlane(live ? ((k0 + kDecRpi * i) * H + n0) * 2 : wend), kNt));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int m = xr + 16 * b;
@@ -113,11 +121,12 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   };
   uint16_t* slot = lds + wave * SLOT;
 
-  f32x4_t acc[NB][4];
+  constexpr int NJ = kDecCols / 16;  // 16-channel MFMA column blocks
+  f32x4_t acc[NB][NJ];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[b][j][e] = 0.f;
 
@@ -126,7 +135,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int g = lane >> 4, s4 = (lane & 15) >> 2, u4 = lane & 3;
   auto use = [&](const Stage& S) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st16(slot + dec_off(wr + 8 * i, wc * 8), S.w[i]);
+    for (int i = 0; i < kDecLoads; ++i) st16(slot + dec_off(wr + kDecRpi * i, wc * 8), S.w[i]);
 #pragma unroll
     for (int b = 0; b < NB; ++b) st16(slot + SE + dec_xoff(xr + 16 * b, xc), S.x[b]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes land before its reads
@@ -134,7 +143,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < NB; ++b) xa[b] = ld16(slot + SE + dec_xoff(16 * b + (lane & 15), lane >> 4));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       u32x4 bv;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -169,18 +178,19 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
 
   // Add the waves' partial products in wave order.  Accumulator layout
   // (16x16): channel 16j + lane%16, token rows 16b + 4*(lane/16) + e.
-  float* red = reinterpret_cast<float*>(lds);  // [4 waves][32 tokens][64 channels] = 32 KiB
+  float* red = reinterpret_cast<float*>(lds);  // [waves][16*NB tokens][kDecCols channels]
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        red[(wave * kDecMaxM + 16 * b + 4 * g + e) * kDecCols + 16 * j + (lane & 15)] = acc[b][j][e];
+        red[(wave * RR + 16 * b + 4 * g + e) * kDecCols + 16 * j + (lane & 15)] = acc[b][j][e];
   __syncthreads();
   // Each thread takes 4 adjacent channels (16 bytes of fp32) of token rows
-  // tid/16, tid/16 + 16, ...
-  const int q = tid & 15, c4 = n0 + 4 * q;
+  // tid/QPR, tid/QPR + kDecThreads/QPR, ...
+  constexpr int QPR = kDecCols / 4;  // 4-channel groups per row
+  const int q = tid % QPR, c4 = n0 + 4 * q;
   const bool inb = c4 < H;  // H is a multiple of 8, so all 4 channels are in range
   const uint32_t mbits = inb ? *reinterpret_cast<const uint32_t*>(mask + c4) : 0u;
   bool syn[4];
@@ -192,10 +202,10 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   constexpr int kSc1 = 1 << 4;
   const __amdgpu_buffer_rsrc_t prs_t = make_rsrc(partial + t * MH, (uint32_t)(MH * 4));
   if (inb) {
-    for (int m = tid >> 4; m < M; m += kDecThreads / 16) {
-      f32x4_t y = *reinterpret_cast<const f32x4_t*>(red + (0 * kDecMaxM + m) * kDecCols + 4 * q);
+    for (int m = tid / QPR; m < M; m += kDecThreads / QPR) {
+      f32x4_t y = *reinterpret_cast<const f32x4_t*>(red + (0 * RR + m) * kDecCols + 4 * q);
 #pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) y += *reinterpret_cast<const f32x4_t*>(red + (w * kDecMaxM + m) * kDecCols + 4 * q);
+      for (int w = 1; w < kDecWaves; ++w) y += *reinterpret_cast<const f32x4_t*>(red + (w * RR + m) * kDecCols + 4 * q);
       const long long off = t * MH + (long long)m * H + c4;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -221,7 +231,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   if (!is_last) return;
   if (tid == 0) __hip_atomic_store(arrivals + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!any_syn) return;
-  for (int m = tid >> 4; m < M; m += kDecThreads / 16) {
+  for (int m = tid / QPR; m < M; m += kDecThreads / QPR) {
     const int voff = (m * H + c4) * 4;
     f32x4_t y;
     for (int u0 = 0; u0 < T; u0 += 8) {  // 8 ranks' loads in flight, then added in rank order

@@ -229,8 +229,8 @@ def test_decode_shared_workspace(ops):
     and the partials region may hold anything on entry."""
     T, Kr, H = 8, 512, 1032
     ws = torch.zeros(ops.fwd_workspace_bytes(T, 32, Kr, H), dtype=torch.uint8, device=G.dev())
-    nblk = (H + 63) // 64
-    cnt_bytes = (nblk * 4 + 255) // 256 * 256  # one int per 64-channel block, padded to 256 bytes
+    nblk = (H + 127) // 128
+    cnt_bytes = (nblk * 4 + 255) // 256 * 256  # one int per 128-channel block, padded to 256 bytes
     ws[cnt_bytes:].fill_(0x7F)  # partials: arbitrary bytes
     for i, M in enumerate((32, 8, 1, 32, 17)):
         _announce(f"decode shared workspace call {i} M={M}")
