@@ -50,10 +50,6 @@ __device__ __forceinline__ int dec_off(int k, int ch) {
   return k * kDecCols + (((ch >> 3) ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 3) + (ch & 7);
 }
 
-// X stage layout [16*NB token rows][32 k], 64-byte rows; 16-byte chunks XOR
-// swizzled by (row / 4) % 4 so the 16 rows of an A-fragment read hit distinct
-// banks.
-__device__ __forceinline__ int dec_xoff(int row, int ch) { return row * kDecStage + ((ch ^ ((row >> 2) & 3)) << 3); }
 
 template <int NB>  // MFMA row blocks of 16 tokens: 1 (M <= 16) or 2
 __global__ void __launch_bounds__(kDecThreads)
@@ -63,8 +59,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
                          int H) {
   constexpr int D = 2;                      // stages held in registers: one being used, one loading
   constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
-  constexpr int XE = 16 * NB * kDecStage;   // X elements per stage (1 or 2 KiB)
-  constexpr int SLOT = SE + XE;             // one LDS slot per wave
+  constexpr int SLOT = SE;                  // one LDS slot per wave
   constexpr int RR = 16 * NB;               // token rows of the fp32 reduction area
   constexpr int LDS = kDecWaves * SLOT > kDecWaves * RR * kDecCols * 2
                           ? kDecWaves * SLOT
@@ -83,17 +78,18 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int nst = (ns_all - wave + kDecWaves - 1) / kDecWaves;
 
   // Operands are loaded into registers D-1 stages ahead (plain buffer loads:
-  // the compiler tracks them and waits exactly), then written to this wave's
-  // LDS slot for the transposing reads.  Per lane and stage: 8 weight pieces
-  // (k-row lane/16 + 4i, 16-byte chunk lane%16) and NB token pieces (token row
-  // lane/4 + 16b, k-chunk lane%4).  Weight rows past Kr, token rows past M and
-  // X columns past Kr read as zero (out of the buffer's range).
+  // the compiler tracks them and waits exactly).  Per lane and stage: 8
+  // weight pieces (k-row lane/16 + 4i, 16-byte chunk lane%16), written to this
+  // wave's LDS slot for the transposing reads, and NB token pieces loaded
+  // straight in the MFMA A-fragment layout (token row lane%16 + 16b, 8-k
+  // chunk lane/16).  Weight rows past Kr, token rows past M and X columns
+  // past Kr read as zero (out of the buffer's range).
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + t * KH, (uint32_t)(KH * 2));
   const uint32_t xbytes = (uint32_t)(MK * 2);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X + t * MK, xbytes);
   const int wr = lane / kDecLpr, wc = lane % kDecLpr;
   const int wvoff = (wr * H + wc * 8) * 2;
-  const int xr = lane >> 2, xc = lane & 3;
+  const int xr = lane & 15, xc = lane >> 4;  // A-fragment layout: token row, 8-k chunk
   struct Stage {
     u32x4 w[kDecLoads];
     u32x4 x[NB];
@@ -136,12 +132,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   auto use = [&](const Stage& S) {
 #pragma unroll
     for (int i = 0; i < kDecLoads; ++i) st16(slot + dec_off(wr + kDecRpi * i, wc * 8), S.w[i]);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) st16(slot + SE + dec_xoff(xr + 16 * b, xc), S.x[b]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes land before its reads
-    u32x4 xa[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) xa[b] = ld16(slot + SE + dec_xoff(16 * b + (lane & 15), lane >> 4));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       u32x4 bv;
@@ -155,7 +146,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
       }
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb)
-        acc[bb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[bb]), as_bf16x8(bv), acc[bb][j], 0, 0, 0);
+        acc[bb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(S.x[bb]), as_bf16x8(bv), acc[bb][j], 0, 0, 0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the slot is rewritten
   };
