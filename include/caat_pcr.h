@@ -29,7 +29,7 @@
  *     an error nothing is enqueued and the status code says why.
  *   - Sizes: 1 <= T <= 64; M >= 0 (M == 0 enqueues nothing, and tensors
  *     with no elements may then be NULL); Kr and H are positive multiples of
- *     8; one rank's slices (M*Kr, Kr*H, M*H elements) stay below 2^31.
+ *     8; one rank's slices (M*Kr, Kr*H, M*H elements) stay below 2^30.
  *     Tensor pointers must be 16-byte aligned, the mask 8-byte aligned.
  *   - Sums of synced channels are taken in fp32, in ascending rank order,
  *     once per element, and the one result is written to every rank, so the

@@ -27,8 +27,8 @@ int check_dims(int T, int M, int Kr, int H) {
   // element counts of the largest tensor must fit the kernels' 64-bit offsets
   // and the grid sizes (<= 2^31 workgroups)
   if ((long long)T * M * (long long)(H > Kr ? H : Kr) > (1LL << 40)) return CAAT_ERR_DIM;
-  // one rank's slices are addressed with 32-bit element offsets
-  const long long lim = 1LL << 31;
+  // one rank's bf16 slices are addressed with 32-bit signed byte offsets
+  const long long lim = 1LL << 30;
   if ((long long)M * Kr >= lim || (long long)Kr * H >= lim || (long long)M * H >= lim) return CAAT_ERR_DIM;
   return CAAT_OK;
 }

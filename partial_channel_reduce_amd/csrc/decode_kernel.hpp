@@ -106,7 +106,8 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
     for (int i = 0; i < kDecLoads; ++i)
       S.w[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     wrs, wvoff, __builtin_amdgcn_readfirstlane(live ? ((k0 + kDecRpi * i) * H + n0) * 2 : wend), kNt));
+                     wrs, wvoff, __builtin_amdgcn_readfirstlane(
+                               live ? (int)(((uint32_t)(k0 + kDecRpi * i) * (uint32_t)H + (uint32_t)n0) * 2u) : wend), kNt));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int m = xr + 16 * b;

@@ -113,7 +113,9 @@ struct KcDma {
 #pragma unroll
     for (int i = 0; i < R / (8 * NW); ++i) {
       const int rb = (i * NW + wave) * 8;  // 8 rows per instruction
-      const int soff = __builtin_amdgcn_readfirstlane(((r0 + rb) * ld + k0) * 2);
+      // byte offsets in unsigned 32-bit arithmetic: rows past the end of the
+      // buffer may take them past 2^31, where they read as zero
+      const int soff = __builtin_amdgcn_readfirstlane((int)(((uint32_t)(r0 + rb) * (uint32_t)ld + (uint32_t)k0) * 2u));
       dma16(rsrc, tile + rb * kBK, voff, soff);
     }
   }
@@ -139,7 +141,7 @@ struct MnDma {
 #pragma unroll
     for (int i = 0; i < R / (8 * NW); ++i) {
       const int kb = (i * NW + wave) * RPI;
-      const int soff = __builtin_amdgcn_readfirstlane(((k0 + kb) * ld + c0) * 2);
+      const int soff = __builtin_amdgcn_readfirstlane((int)(((uint32_t)(k0 + kb) * (uint32_t)ld + (uint32_t)c0) * 2u));
       dma16(rsrc, tile + kb * R, voff, soff);
     }
   }

@@ -86,8 +86,9 @@ def test_fwd_validation(L):
     assert fwd(L, mask=C + 4) == ALIGN
     assert fwd(L, out=A) == ALIAS  # out over X
     assert fwd(L, out=B + 16) == ALIAS  # out over W
-    # per-rank slice beyond 32-bit element offsets
+    # per-rank slice beyond 32-bit signed byte offsets (2^30 elements)
     assert fwd(L, T=1, M=1 << 20, Kr=4096, H=64) == DIM
+    assert fwd(L, T=1, M=1 << 18, Kr=4096, H=64) == DIM
     # decode-shaped call without its workspace
     assert fwd(L, M=8) == WS
     need = L.caat_rowpar_pcr_fwd_workspace_bytes(8, 8, 64, 64)
