@@ -6,17 +6,17 @@
 //   rowpar_pcr_decode_kernel: one workgroup per (rank t, 128-channel block),
 //     so every weight row piece it reads is 256 contiguous bytes.  Its 8 waves
 //     split the contraction (interleaved 32-row stages); each keeps two
-//     32-row x 128-channel weight stages (and the matching 32 columns of X_t's
-//     token rows) loading into registers, and writes each stage through its
-//     own small LDS slot into 16x16x32 bf16 MFMAs, the weights via gfx950's
-//     LDS transpose read.  (Plain loads into registers stream faster here
+//     32-row x 128-channel weight stages loading into registers, writes each
+//     stage to its own LDS slot and feeds it to 16x16x32 bf16 MFMAs through
+//     gfx950's LDS transpose read; X_t's token rows are loaded straight in the
+//     MFMA operand layout.  (Plain loads into registers stream faster here
 //     than copies straight into LDS; with the MFMAs removed the kernel is no
-//     faster: it is bound by the weight stream.)  The waves' partial sums are added in wave order through
-//     LDS; local channels are written to out[t] as bf16, synced channels
-//     leave their fp32 value in the workspace.  The last of the T workgroups
-//     of a channel block to finish (an arrival counter per block, in the
-//     workspace) adds the synced values in ascending rank order and writes
-//     the one bf16 result to every rank.
+//     faster: it is bound by the weight stream.)  The waves' partial sums are
+//     added in wave order through LDS; local channels are written to out[t]
+//     as bf16, synced channels leave their fp32 value in the workspace.  The
+//     last of the T workgroups of a channel block to finish (an arrival
+//     counter per block, in the workspace) adds the synced values in
+//     ascending rank order and writes the one bf16 result to every rank.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -34,22 +34,13 @@ constexpr int kDecLoads = kDecStage / kDecRpi;  // weight loads per stage
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-}
-
 // LDS stage layout [32 k][128 channels], 256-byte rows (one pass over the 64
 // banks each); 16-byte chunks XOR swizzled by 2*(k%4) + 8*((k/8)%2): a
 // transpose read serves 32 lanes at a time, k-rows {k..k+3} and {k+8..k+11}
-// of two 16-channel pieces, which this spreads over all 64 banks.
+// of one 16-channel block, which this spreads over all 64 banks.
 __device__ __forceinline__ int dec_off(int k, int ch) {
   return k * kDecCols + (((ch >> 3) ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 3) + (ch & 7);
 }
-
 
 template <int NB>  // MFMA row blocks of 16 tokens: 1 (M <= 16) or 2
 __global__ void __launch_bounds__(kDecThreads)

@@ -16,9 +16,8 @@
 //            ds_read_b64_tr_b16 (gfx950's LDS transpose read: within each
 //            16-lane group, lane 4s+u names 4 consecutive rows of k-row s, and
 //            every lane receives one row's values from the 4 k-rows).
-// Plain operands are copied global -> LDS with buffer_load_dwordx4 ... lds (no
-// register staging); operands that need a per-element select are staged
-// through registers and written with ds_write_b128.
+// Every operand is copied global -> LDS with buffer_load_dwordx4 ... lds (no
+// register staging).
 #pragma once
 
 #include "common.hpp"
