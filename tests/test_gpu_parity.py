@@ -144,6 +144,8 @@ INT_CASES = [
     (1, 70, 64, 128, "random", 0.5),     # T = 1
     (20, 5, 64, 136, "random", 0.5),     # M <= 32, T = 20
     (3, 17, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
+    (1, 3, 64, 136, "random", 0.5),      # decode, T = 1 (every workgroup arrives last)
+    (13, 17, 40, 264, "strided", 0.5),   # decode, T = 13, two token blocks
 ]
 
 
