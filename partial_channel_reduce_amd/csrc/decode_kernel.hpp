@@ -12,11 +12,13 @@
 //     MFMA operand layout.  (Plain loads into registers stream faster here
 //     than copies straight into LDS; with the MFMAs removed the kernel is no
 //     faster: it is bound by the weight stream.)  The waves' partial sums are
-//     added in wave order through LDS; local channels are written to out[t]
-//     as bf16, synced channels leave their fp32 value in the workspace.  The
-//     last of the T workgroups of a channel block to finish (an arrival
-//     counter per block, in the workspace) adds the synced values in
-//     ascending rank order and writes the one bf16 result to every rank.
+//     added in wave order through LDS.  A channel block with no synced channel
+//     is written straight to out[t]; otherwise each workgroup leaves its fp32
+//     values in the workspace, and the last of the T workgroups of the block
+//     to finish (an arrival counter per block, in the workspace) adds the
+//     synced values in ascending rank order and writes every rank's output
+//     (the one bf16 sum on synced channels, the rank's own value elsewhere)
+//     with whole 8-byte stores.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -171,40 +173,61 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
         red[(wave * RR + 16 * b + 4 * g + e) * kDecCols + 16 * j + (lane & 15)] = acc[b][j][e];
   __syncthreads();
   // Each thread takes 4 adjacent channels (16 bytes of fp32) of token rows
-  // tid/QPR, tid/QPR + kDecThreads/QPR, ...
-  constexpr int QPR = kDecCols / 4;  // 4-channel groups per row
-  const int q = tid % QPR, c4 = n0 + 4 * q;
+  // tid/QPR + RPP*p, p = 0 .. NP-1.
+  constexpr int QPR = kDecCols / 4;          // 4-channel groups per row
+  constexpr int RPP = kDecThreads / QPR;     // token rows per pass
+  constexpr int NP = (RR + RPP - 1) / RPP;   // passes covering 16*NB rows
+  const int q = tid % QPR, c4 = n0 + 4 * q, mt = tid / QPR;
   const bool inb = c4 < H;  // H is a multiple of 8, so all 4 channels are in range
   const uint32_t mbits = inb ? *reinterpret_cast<const uint32_t*>(mask + c4) : 0u;
   bool syn[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) syn[e] = ((mbits >> (8 * e)) & 0xffu) != 0;
-  const bool any_syn = syn[0] | syn[1] | syn[2] | syn[3];
-  // fp32 partials of rank t, [M][H]: written and read with device-scope
-  // coherent (sc1) 16-byte accesses.
-  constexpr int kSc1 = 1 << 4;
-  const __amdgpu_buffer_rsrc_t prs_t = make_rsrc(partial + t * MH, (uint32_t)(MH * 4));
-  if (inb) {
-    for (int m = tid / QPR; m < M; m += kDecThreads / QPR) {
-      f32x4_t y = *reinterpret_cast<const f32x4_t*>(red + (0 * RR + m) * kDecCols + 4 * q);
+  f32x4_t y[NP];
 #pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) y += *reinterpret_cast<const f32x4_t*>(red + (w * RR + m) * kDecCols + 4 * q);
-      const long long off = t * MH + (long long)m * H + c4;
+  for (int p = 0; p < NP; ++p) {
+    const int m = mt + RPP * p;
+    if (m < M) {
+      y[p] = *reinterpret_cast<const f32x4_t*>(red + (0 * RR + m) * kDecCols + 4 * q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!syn[e]) out[off + e] = f32_to_bf16(y[e]);
-      if (any_syn)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), prs_t, (m * H + c4) * 4, 0, kSc1);
+      for (int w = 1; w < kDecWaves; ++w) y[p] += *reinterpret_cast<const f32x4_t*>(red + (w * RR + m) * kDecCols + 4 * q);
     }
   }
+  // bf16 output of 4 channels of token row m of rank u: one 8-byte store.
+  auto put = [&](int u, int m, f32x4_t v) {
+    u32x2 pk;
+    pk[0] = pack_bf16x2(v[0], v[1]);
+    pk[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(out + u * MH + (long long)m * H + c4) = pk;
+  };
+  // A channel block without synced channels (the same for all T workgroups
+  // of the block) needs no exchange: each rank writes its own values.
+  if (!__syncthreads_or(mbits != 0u)) {
+    if (inb)
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        if (mt + RPP * p < M) put(t, mt + RPP * p, y[p]);
+    return;
+  }
 
-  // The T workgroups of one channel block (one per rank) each publish their
-  // synced fp32 values, then count themselves in; the last to arrive adds
-  // the T values in ascending rank order, writes the one bf16 result to every
-  // rank and returns the counter to zero for the next call.  The partials
-  // and the counter use device-scope coherent accesses, which need no cache
-  // write-back or invalidation across the chip's L2 slices: waiting for the
-  // stores' acknowledgement before the arrival is counted orders them.
+  // Otherwise every workgroup publishes its fp32 values [M][128] of rank t
+  // (device-scope coherent sc1 16-byte stores) and counts itself in; the
+  // last of the T to arrive reads all T ranks' values, adds them in
+  // ascending rank order on the synced channels and writes every rank's
+  // output: the sum on synced channels, the rank's own value elsewhere.
+  // Waiting for the stores' acknowledgement before the arrival is counted
+  // orders them; the coherent accesses need no cache write-back or
+  // invalidation across the chip's L2 slices.
+  constexpr int kSc1 = 1 << 4;
+  auto prs = [&](int u) { return make_rsrc(partial + u * MH, (uint32_t)(MH * 4)); };
+  if (inb) {
+    const __amdgpu_buffer_rsrc_t r = prs(t);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int m = mt + RPP * p;
+      if (m < M) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y[p]), r, (m * H + c4) * 4, 0, kSc1);
+    }
+  }
   __shared__ int is_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -213,27 +236,51 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   __syncthreads();
   if (!is_last) return;
   if (tid == 0) __hip_atomic_store(arrivals + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!any_syn) return;
-  for (int m = tid / QPR; m < M; m += kDecThreads / QPR) {
-    const int voff = (m * H + c4) * 4;
-    f32x4_t y;
-    for (int u0 = 0; u0 < T; u0 += 8) {  // 8 ranks' loads in flight, then added in rank order
-      f32x4_t v[8];
+  if (!inb) return;
+  // Ranks are taken 8 at a time, all their loads (every pass) in flight
+  // together; with T <= 8 the loaded values also give the local channels.
+  auto sel = [&](f32x4_t a, f32x4_t b) {  // synced channels from a, the rest from b
+    f32x4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = syn[e] ? a[e] : b[e];
+    return r;
+  };
+  for (int u0 = 0; u0 < T; u0 += 8) {
+    f32x4_t v[NP][8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (u0 + k < T) {
+        const __amdgpu_buffer_rsrc_t r = prs(u0 + k);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int m = mt + RPP * p;
+          if (m < M) v[p][k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (m * H + c4) * 4, 0, kSc1));
+        }
+      }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (u0 + k < T)
-          v[k] = __builtin_bit_cast(
-              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(partial + (u0 + k) * MH, (uint32_t)(MH * 4)), voff, 0, kSc1));
+        if (u0 + k < T) y[p] = (u0 + k == 0) ? v[p][k] : y[p] + v[p][k];
+    if (T <= 8) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (u0 + k < T) y = (u0 + k == 0) ? v[k] : y + v[k];
-    }
-    for (int u = 0; u < T; ++u) {
-      const long long off = u * MH + (long long)m * H + c4;
+      for (int p = 0; p < NP; ++p) {
+        const int m = mt + RPP * p;
+        if (m < M)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (syn[e]) out[off + e] = f32_to_bf16(y[e]);
+          for (int k = 0; k < 8; ++k)
+            if (k < T) put(k, m, sel(y[p], v[p][k]));
+      }
+      return;
     }
+  }
+  // More than 8 ranks: a second pass re-reads each rank's own values.
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int m = mt + RPP * p;
+    if (m < M)
+      for (int u = 0; u < T; ++u)
+        put(u, m, sel(y[p], __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs(u), (m * H + c4) * 4, 0, kSc1))));
   }
 }
 

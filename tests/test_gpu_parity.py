@@ -146,6 +146,11 @@ INT_CASES = [
     (3, 17, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
     (1, 3, 64, 136, "random", 0.5),      # decode, T = 1 (every workgroup arrives last)
     (13, 17, 40, 264, "strided", 0.5),   # decode, T = 13, two token blocks
+    (8, 1, 1376, 4096, "prefix", 0.5),   # decode: all-synced and all-local channel blocks
+    (8, 32, 256, 1024, "prefix", 0.25),  # decode, M = 32, block-uniform mask
+    (4, 5, 64, 200, "prefix", 0.0),      # decode, nothing synced (no exchange), ragged block
+    (4, 9, 64, 200, "prefix", 1.0),      # decode, everything synced, ragged block
+    (13, 20, 40, 392, "prefix", 0.5),    # decode, T = 13, one mixed block between uniform ones
 ]
 
 
