@@ -12,6 +12,8 @@
 // order and write whole lines with 16-byte stores.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "reduce_kernels.hpp"
 
@@ -255,23 +257,38 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W
     db.load<BN, NW>(H, m0, c * kBK, buf + BM * kBK, wave);
   };
 
-  issue(0);
-  for (int c = 0; c < nk; ++c) {
-    uint16_t* As = smem + (c & 1) * S::BUF;
-    uint16_t* Bs = As + BM * kBK;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (c == nk - 1 && kv_last < kBK) {  // channels past H: the next row's values
-      zero_kcont_tail<BM, S::THREADS>(As, kv_last, tid);
-      zero_kcont_tail<BN, S::THREADS>(Bs, kv_last, tid);
+  // A wave whose rows of dX_t^T all lie past Kr (the last column tile when
+  // Kr is not a multiple of BM) only issues its share of the copies.  Waves
+  // with the same wm sit on different SIMDs, so the idle ones free half of
+  // every SIMD's matrix-core time in such a tile.
+  // (The two kinds of wave run separate copies of the loop, with the same
+  // barriers, so that neither carries the other's registers.)
+  auto loop = [&](auto compute) {
+    issue(0);
+    for (int c = 0; c < nk; ++c) {
+      uint16_t* As = smem + (c & 1) * S::BUF;
+      uint16_t* Bs = As + BM * kBK;
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (c == nk - 1 && kv_last < kBK) {  // channels past H: the next row's values
+        zero_kcont_tail<BM, S::THREADS>(As, kv_last, tid);
+        zero_kcont_tail<BN, S::THREADS>(Bs, kv_last, tid);
+        __syncthreads();
+      }
+      if constexpr (decltype(compute)::value)
+        mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_kcont(As, wm * S::WM + i * 32, ks, lane); },
+                          [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                          [&] {
+                            if (c + 1 < nk) issue(c + 1);
+                          });
+      else if (c + 1 < nk)
+        issue(c + 1);
     }
-    mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_kcont(As, wm * S::WM + i * 32, ks, lane); },
-                      [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
-                      [&] {
-                        if (c + 1 < nk) issue(c + 1);
-                      });
-  }
+  };
+  if (k0r + wm * S::WM < Kr)
+    loop(std::true_type{});
+  else
+    loop(std::false_type{});
 
   // Stage the transposed sub-tile through LDS and write whole rows of dX_t.
   using RS = RowStage<S::WM>;
@@ -307,7 +324,10 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  // wn = wave / 2: the two waves of each SIMD (wave and wave + 4 with eight
+  // waves) take different row ranges of dW_t, so when the last row tile
+  // leaves the upper waves idle (below) every SIMD keeps one busy wave.
+  const int wm = wave % S::WGM, wn = wave / S::WGM;
   const int per_rank = tiles_m * tiles_n;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int t = lin / per_rank;
@@ -328,18 +348,29 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
     db.template load<NW>(Kr, k0r, c * kBK, buf + BM * kBK, wave);
   };
 
-  issue(0);
-  for (int c = 0; c < nk; ++c) {
-    uint16_t* As = smem + (c & 1) * S::BUF;
-    uint16_t* Bs = As + BM * kBK;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
-                      [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
-                      [&] {
-                        if (c + 1 < nk) issue(c + 1);
-                      });
-  }
+  // A wave whose rows of dW_t all lie past Kr (the last row tile when Kr is
+  // not a multiple of BN) only issues its share of the copies.
+  auto loop = [&](auto compute) {
+    issue(0);
+    for (int c = 0; c < nk; ++c) {
+      uint16_t* As = smem + (c & 1) * S::BUF;
+      uint16_t* Bs = As + BM * kBK;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if constexpr (decltype(compute)::value)
+        mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
+                          [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                          [&] {
+                            if (c + 1 < nk) issue(c + 1);
+                          });
+      else if (c + 1 < nk)
+        issue(c + 1);
+    }
+  };
+  if (k0r + wn * S::WN < Kr)
+    loop(std::true_type{});
+  else
+    loop(std::false_type{});
 
   // Stage the transposed sub-tile through LDS and write whole rows of dW_t.
   using RS = RowStage<S::WM>;
