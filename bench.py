@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
+    ap.add_argument("--rocprof-mfma", metavar="DIR",
+                    help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
+                         "--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 csv run of the train leg, and exit")
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
                          "calibrated against the copy leg's kernel, and exit")
@@ -70,6 +73,9 @@ def main():
     args = parse()
     if args.rocprof_stats:
         print(rocprof_stats_summary(args.rocprof_stats))
+        return
+    if args.rocprof_mfma:
+        print(rocprof_mfma_summary(args.rocprof_mfma))
         return
     if args.rocprof_traffic:
         print(rocprof_traffic_summary(*args.rocprof_traffic))
@@ -386,6 +392,26 @@ def rocprof_stats_summary(d: str) -> str:
         out.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def rocprof_mfma_summary(d: str) -> str:
+    """Per-kernel MFMA busy fraction (MfmaUtil: MFMA busy cycles over all SIMDs'
+    active cycles) and performed bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16
+    x 512) per dispatch, the latter beside the GEMM's algorithmic 2*M*K*H."""
+    acc = {}
+    for r in _read_csv(_find(d, "counter_collection.csv")):
+        acc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    algo = 2.0 * M * (T * KR) * H
+    out = ["| kernel | dispatches | MfmaUtil % | MFMA GFLOP per dispatch | / algorithmic 2MKH |",
+           "|---|---|---|---|---|"]
+    for k in sorted({k for k, _ in acc}):
+        util = acc.get((k, "MfmaUtil"))
+        mops = acc.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        if not util or not mops or max(mops) == 0:
+            continue
+        fl = sum(mops) / len(mops) * 512
+        out.append(f"| {_short(k)} | {len(util)} | {sum(util) / len(util):.1f} | {fl / 1e9:.1f} | {fl / algo:.3f} |")
     return "\n".join(out)
 
 
