@@ -43,20 +43,26 @@ def _gather(t, *idx):
 
 
 @pytest.mark.parametrize(
-    "name,T,M,Kr,H,kind",
+    "name,T,M,Kr,H,kind,p",
     [
-        ("Llama2-7B down-proj", 8, 16384, 1376, 4096, "random"),
-        ("Llama2-7B down-proj, S = first half", 8, 16384, 1376, 4096, "prefix"),
-        ("Llama2-7B out-proj", 8, 16384, 512, 4096, "random"),
-        ("TinyLlama-1.1B down-proj", 8, 32768, 704, 2048, "strided"),
-        ("130M down-proj", 8, 8192, 384, 768, "random"),
-        ("130M out-proj", 8, 8192, 96, 768, "random"),
+        ("Llama2-7B down-proj", 8, 16384, 1376, 4096, "random", 0.5),
+        ("Llama2-7B down-proj, S = first half", 8, 16384, 1376, 4096, "prefix", 0.5),
+        ("Llama2-7B out-proj", 8, 16384, 512, 4096, "random", 0.5),
+        ("TinyLlama-1.1B down-proj", 8, 32768, 704, 2048, "strided", 0.5),
+        ("TinyLlama-1.1B down-proj, S = first half", 8, 32768, 704, 2048, "prefix", 0.5),
+        ("TinyLlama-1.1B out-proj", 8, 32768, 256, 2048, "strided", 0.5),
+        ("130M down-proj", 8, 8192, 384, 768, "random", 0.5),
+        ("130M out-proj", 8, 8192, 96, 768, "random", 0.5),
+        ("130M down-proj, p = 0", 8, 8192, 384, 768, "random", 0.0),
+        ("130M down-proj, p = 0.25", 8, 8192, 384, 768, "random", 0.25),
+        ("130M out-proj, p = 0.75", 8, 8192, 96, 768, "random", 0.75),
+        ("130M out-proj, p = 1", 8, 8192, 96, 768, "random", 1.0),
     ],
 )
-def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind):
+def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
     _announce(f"full-size fwd {name}")
     X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=1)
-    mask = synth.make_mask(H, 0.5, kind, seed=1)
+    mask = synth.make_mask(H, p, kind, seed=1)
     Xd, Wd, mk = G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask)
     out = ops.rowpar_pcr_fwd(Xd, Wd, mk)
     out2 = ops.rowpar_pcr_fwd(Xd, Wd, mk)
@@ -73,13 +79,23 @@ def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind):
     _check_sampled_bf16(got, ref, mask[cs] != 0, f"fwd {name}")
 
 
-@pytest.mark.parametrize("kind", ["random", "prefix"])
-def test_bwd_7b_full_size_sampled(ops, kind):
-    T, M, Kr, H = 8, 16384, 1376, 4096
-    _announce(f"full-size bwd Llama2-7B down-proj, {kind} mask")
+@pytest.mark.parametrize(
+    "name,T,M,Kr,H,kind,p",
+    [
+        ("Llama2-7B down-proj", 8, 16384, 1376, 4096, "random", 0.5),
+        ("Llama2-7B down-proj, S = first half", 8, 16384, 1376, 4096, "prefix", 0.5),
+        ("Llama2-7B out-proj", 8, 16384, 512, 4096, "random", 0.5),
+        ("TinyLlama-1.1B down-proj", 8, 32768, 704, 2048, "strided", 0.5),
+        ("TinyLlama-1.1B out-proj", 8, 32768, 256, 2048, "prefix", 0.5),
+        ("130M down-proj, p = 0.25", 8, 8192, 384, 768, "random", 0.25),
+        ("130M out-proj, p = 0.75", 8, 8192, 96, 768, "random", 0.75),
+    ],
+)
+def test_bwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
+    _announce(f"full-size bwd {name}")
     X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=2)
     dZ = synth.make_grad(T, M, H, seed=2)
-    mask = synth.make_mask(H, 0.5, kind, seed=2)
+    mask = synth.make_mask(H, p, kind, seed=2)
     args = (G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
     dX, dW = ops.pcr_bwd(*args)
     dX2, dW2 = ops.pcr_bwd(*args)
@@ -89,18 +105,19 @@ def test_bwd_7b_full_size_sampled(ops, kind):
     rng = np.random.default_rng(8)
     ts, ms, ks = _samples(rng, NSAMPLE, T, M, Kr)
     ref = oracle.bwd_dx_at(dZ, W, mask, ts, ms, ks)
-    G.check_bf16(oracle.bf16_to_f64(_gather(dX, ts, ms, ks)), ref, None, "dX 7B")
+    G.check_bf16(oracle.bf16_to_f64(_gather(dX, ts, ms, ks)), ref, None, f"dX {name}")
     ts, ks, cs = _samples(rng, 256, T, Kr, H)
     ref = oracle.bwd_dw_at(dZ, X, mask, ts, ks, cs)
-    G.check_bf16(oracle.bf16_to_f64(_gather(dW, ts, ks, cs)), ref, mask[cs] != 0, "dW 7B")
+    G.check_bf16(oracle.bf16_to_f64(_gather(dW, ts, ks, cs)), ref, mask[cs] != 0, f"dW {name}")
 
 
+@pytest.mark.parametrize("Kr", [1376, 512])
 @pytest.mark.parametrize("M", [1, 8, 32])
-def test_decode_7b_full_size(ops, M):
-    """Decode-shaped forward on the 7B down-proj: complete comparison (the
-    oracle finishes these sizes quickly)."""
-    T, Kr, H = 8, 1376, 4096
-    _announce(f"full-size decode M={M}")
+def test_decode_7b_full_size(ops, M, Kr):
+    """Decode-shaped forward on the 7B down-proj (Kr = 1376) and out-proj
+    (Kr = 512): complete comparison (the oracle finishes these sizes quickly)."""
+    T, H = 8, 4096
+    _announce(f"full-size decode M={M} Kr={Kr}")
     X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=3)
     mask = synth.make_mask(H, 0.5, "random", seed=3)
     out = ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
