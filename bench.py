@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -97,7 +97,7 @@ def main():
     ops.lib()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode"}
+    legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -264,6 +264,14 @@ def main():
             red[f"M{Mr}"] = {"us": round(t * 1e3, 2), "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "bound": "latency"}
             del sets, outs
         res["reduce_only_f32"] = red
+        # bf16 variant (the form the backward uses for G), out of place
+        Yb = randn_bf16((T, 16384, H))
+        ob = torch.empty_like(Yb)
+        t = time_call(lambda: ops.partial_channel_reduce(Yb, mk, out=ob), 10)
+        gbs = 2.0 * T * 16384 * H * 2 / (t * 1e-3) / 1e9
+        res["reduce_only_bf16"] = {"M16384": {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
+                                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}}
+        del Yb, ob
         torch.cuda.empty_cache()
 
     # -------------------------------------------------- decode-shaped forward
@@ -290,6 +298,30 @@ def main():
         res["decode_down_proj"] = dec
         del Ws
         torch.cuda.empty_cache()
+
+    # ------------------------------------------------ tensor-parallel sweep
+    if "tsweep" in legs:
+        # The same layer (M = 16384, K = 11008, H = 4096, p = 0.5 random mask)
+        # split over T = 2, 4, 8, 16 ranks: Kr = K / T; the product's flops
+        # stay 2MKH, the output (and the synced payload) grow with T.
+        sweep = {}
+        mk = mask_dev(H)
+        K_all = T * KR
+        for Ts in (2, 4, 8, 16):
+            Krs = K_all // Ts
+            Xs = randn_bf16((Ts, M, Krs))
+            Ws = randn_bf16((Ts, Krs, H), 0.02)
+            dZs = randn_bf16((Ts, M, H))
+            outs = torch.empty((Ts, M, H), dtype=torch.bfloat16, device=dev)
+            dXs, dWs = torch.empty_like(Xs), torch.empty_like(Ws)
+            wss = torch.empty(ops.bwd_workspace_bytes(Ts, M, Krs, H), dtype=torch.uint8, device=dev)
+            tf = time_call(lambda: ops.rowpar_pcr_fwd(Xs, Ws, mk, out=outs), 5)
+            tb = time_call(lambda: ops.pcr_bwd(dZs, Xs, Ws, mk, dX=dXs, dW=dWs, workspace=wss), 5)
+            sweep[f"T{Ts}"] = {"Kr": Krs, "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+                               "tflops": round(flops_step / ((tf + tb) * 1e-3) / 1e12, 2)}
+            del Xs, Ws, dZs, outs, dXs, dWs, wss
+            torch.cuda.empty_cache()
+        res["t_sweep"] = sweep
 
     # ------------------------------------------- copy of known size (counters)
     if "copy" in legs:
@@ -340,6 +372,8 @@ def main():
         "library_gemm": res.get("library_gemm"),
         "out_proj": res.get("out_proj"),
         "reduce_only_f32": res.get("reduce_only_f32"),
+        "reduce_only_bf16": res.get("reduce_only_bf16"),
+        "t_sweep": res.get("t_sweep"),
         "decode_down_proj": res.get("decode_down_proj"),
         "copy": res.get("copy"),
         "src": src_hash(),

@@ -57,6 +57,9 @@ def _gather(t, *idx):
         ("130M down-proj, p = 0.25", 8, 8192, 384, 768, "random", 0.25),
         ("130M out-proj, p = 0.75", 8, 8192, 96, 768, "random", 0.75),
         ("130M out-proj, p = 1", 8, 8192, 96, 768, "random", 1.0),
+        ("Llama2-7B down-proj over 2 ranks", 2, 16384, 5504, 4096, "random", 0.5),
+        ("Llama2-7B down-proj over 4 ranks", 4, 16384, 2752, 4096, "random", 0.5),
+        ("Llama2-7B down-proj over 16 ranks", 16, 16384, 688, 4096, "random", 0.5),
     ],
 )
 def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
@@ -89,6 +92,8 @@ def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
         ("TinyLlama-1.1B out-proj", 8, 32768, 256, 2048, "prefix", 0.5),
         ("130M down-proj, p = 0.25", 8, 8192, 384, 768, "random", 0.25),
         ("130M out-proj, p = 0.75", 8, 8192, 96, 768, "random", 0.75),
+        ("Llama2-7B down-proj over 2 ranks", 2, 16384, 5504, 4096, "random", 0.5),
+        ("Llama2-7B down-proj over 16 ranks", 16, 16384, 688, 4096, "random", 0.5),
     ],
 )
 def test_bwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
