@@ -25,10 +25,15 @@ Readings of points the pages leave open (the reduce is a SUM; local channels
 are not rescaled; the layer has no bias; forward and backward use the same
 S; the incoming gradient differs per rank) are listed with the design notes.
 
+The layer that consumes the reduce's output, a column-parallel product, now
+takes a different input on every rank; colpar_fwd / colpar_bwd define it and
+its exact backward, whose input gradient stays on its rank.
+
 Every function here is pinned by the CPU tests to something other than
 itself: a message-passing simulation of the restricted all-reduce on integer
 inputs, the un-sharded layer (all channels synced), the per-rank layer (no
-channel synced), the adjoint identity and finite differences.
+channel synced), the adjoint identity and finite differences (of the layer
+alone and of the two-layer chain with the column-parallel product).
 """
 from __future__ import annotations
 
@@ -41,6 +46,8 @@ __all__ = [
     "rowpar_partials",
     "rowpar_pcr_fwd",
     "pcr_bwd",
+    "colpar_fwd",
+    "colpar_bwd",
     "fwd_at",
     "bwd_dx_at",
     "bwd_dw_at",
@@ -111,6 +118,33 @@ def pcr_bwd(dZ, X, W, mask):
     dX = np.stack([G[t] @ W[t].T for t in range(T)])
     dW = np.stack([X[t].T @ G[t] for t in range(T)])
     return dX, dW
+
+
+def colpar_fwd(A, W) -> np.ndarray:
+    """Column-parallel product on per-rank inputs: U[t] = A[t] @ W[t] -> [T,M,N].
+
+    After the partial channel-reduce each rank holds its own activation, so
+    the next layer's column-parallel product multiplies rank t's activation
+    A[t] [M,K] by rank t's column slice W[t] [K,N]."""
+    A = bf16_to_f64(A)
+    W = bf16_to_f64(W)
+    return np.stack([A[t] @ W[t] for t in range(A.shape[0])])
+
+
+def colpar_bwd(dU, A, W):
+    """Exact backward of colpar_fwd for per-rank incoming gradients dU[T,M,N]:
+        dA[t] = dU[t] @ W[t].T     [M,K]
+        dW[t] = A[t].T @ dU[t]     [K,N]
+    A[t] is rank t's own input, so its gradient stays with rank t (no sum over
+    ranks here); in the two-layer chain the only cross-rank sum is pcr_bwd's,
+    over the synced channels."""
+    dU = bf16_to_f64(dU)
+    A = bf16_to_f64(A)
+    W = bf16_to_f64(W)
+    T = A.shape[0]
+    dA = np.stack([dU[t] @ W[t].T for t in range(T)])
+    dW = np.stack([A[t].T @ dU[t] for t in range(T)])
+    return dA, dW
 
 
 # ---------------------------------------------------------------------------

@@ -219,3 +219,85 @@ def check_finite_differences(fwd, bwd, seed=7):
             Wm[idx] -= 1.0
             fd = (loss(X, Wp) - loss(X, Wm)) / 2.0
             assert fd == dW[idx], ("dW", idx, fd, dW[idx])
+
+
+# ---------------------------------------------------------------------------
+# The two-layer chain: the row-parallel layer with partial channel-reduce,
+# then a column-parallel product that takes each rank's own (now different)
+# activation.  Introduction: forward and backward must agree; the ordinary
+# tensor-parallel backward, which sums the column-parallel layer's input
+# gradient over the ranks because that input is replicated, does not.
+# ---------------------------------------------------------------------------
+
+def _concat_ranks(A, axis):
+    return np.concatenate([A[t] for t in range(A.shape[0])], axis=axis)
+
+
+def check_two_layer_finite_differences(fwd, bwd, colfwd, colbwd, seed=9):
+    """Chained backward (colbwd, then bwd on its input gradient) = gradient
+    of L(X, W, W1) = sum(colfwd(fwd(X, W), W1) * C).  L is linear in each of
+    X, W and W1, so the central difference with step 1 is exact on integer
+    inputs; every entry of dX, dW and dW1 is checked."""
+    rng = np.random.default_rng(seed)
+    for T, M, Kr, H, N in ((2, 2, 2, 4, 3), (3, 2, 2, 5, 2), (4, 2, 1, 4, 2)):
+        X = rng.integers(-2, 3, size=(T, M, Kr)).astype(np.float64)
+        W = rng.integers(-2, 3, size=(T, Kr, H)).astype(np.float64)
+        W1 = rng.integers(-2, 3, size=(T, H, N)).astype(np.float64)
+        C = rng.integers(-2, 3, size=(T, M, N)).astype(np.float64)
+        mask = (rng.random(H) < 0.5).astype(np.uint8)
+        mask[0], mask[-1] = 1, 0  # at least one channel of each kind
+
+        def loss(Xa, Wa, W1a):
+            return float(np.sum(colfwd(fwd(Xa, Wa, mask), W1a) * C))
+
+        dZ, dW1 = colbwd(C, fwd(X, W, mask), W1)
+        dX, dW = bwd(dZ, X, W, mask)
+        for name, arr, grad in (("dX", X, dX), ("dW", W, dW), ("dW1", W1, dW1)):
+            for idx in np.ndindex(*arr.shape):
+                p, m = arr.copy(), arr.copy()
+                p[idx] += 1.0
+                m[idx] -= 1.0
+                args_p = [X, W, W1]
+                args_m = [X, W, W1]
+                k = ("dX", "dW", "dW1").index(name)
+                args_p[k], args_m[k] = p, m
+                fd = (loss(*args_p) - loss(*args_m)) / 2.0
+                assert fd == grad[idx], (name, (T, M, Kr, H, N), idx, fd, grad[idx])
+
+
+def check_two_layer_all_synced_is_vanilla(fwd, bwd, colfwd, colbwd, seed=10):
+    """All channels synced: the chain is the un-sharded two-layer product
+    U_full = X_full W_full W1_full, whose gradients are the textbook ones:
+    d X_full = C_full W1_full^T W_full^T, d W_full = X_full^T (C_full W1_full^T),
+    d W1_full = (X_full W_full)^T C_full (each rank holds its slices)."""
+    rng = np.random.default_rng(seed)
+    for T, M, Kr, H, N in ((2, 5, 3, 6, 4), (4, 3, 2, 8, 3), (8, 2, 2, 5, 2)):
+        X = rng.standard_normal((T, M, Kr))
+        W = rng.standard_normal((T, Kr, H))
+        W1 = rng.standard_normal((T, H, N))
+        C = rng.standard_normal((T, M, N))
+        mask = np.ones(H, dtype=np.uint8)
+        dZ, dW1 = colbwd(C, fwd(X, W, mask), W1)
+        dX, dW = bwd(dZ, X, W, mask)
+        Xf, Wf = _concat_ranks(X, 1), _concat_ranks(W, 0)
+        W1f, Cf = _concat_ranks(W1, 1), _concat_ranks(C, 1)
+        Gf = Cf @ W1f.T
+        np.testing.assert_allclose(_concat_ranks(dX, 1), Gf @ Wf.T, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(_concat_ranks(dW, 0), Xf.T @ Gf, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(_concat_ranks(dW1, 1), (Xf @ Wf).T @ Cf, rtol=1e-11, atol=1e-11)
+
+
+def check_two_layer_none_synced_is_ensemble(fwd, bwd, colfwd, colbwd, seed=11):
+    """No channel synced: T independent two-layer products, dX[t] = C[t] W1[t]^T W[t]^T."""
+    rng = np.random.default_rng(seed)
+    for T, M, Kr, H, N in ((2, 5, 3, 6, 4), (4, 3, 2, 8, 3)):
+        X = rng.standard_normal((T, M, Kr))
+        W = rng.standard_normal((T, Kr, H))
+        W1 = rng.standard_normal((T, H, N))
+        C = rng.standard_normal((T, M, N))
+        mask = np.zeros(H, dtype=np.uint8)
+        np.testing.assert_allclose(colfwd(fwd(X, W, mask), W1), np.matmul(np.matmul(X, W), W1), rtol=1e-11, atol=1e-11)
+        dZ, _ = colbwd(C, fwd(X, W, mask), W1)
+        dX, _ = bwd(dZ, X, W, mask)
+        want = np.matmul(np.matmul(C, np.transpose(W1, (0, 2, 1))), np.transpose(W, (0, 2, 1)))
+        np.testing.assert_allclose(dX, want, rtol=1e-11, atol=1e-11)

@@ -230,6 +230,52 @@ def test_reduce_pins_reject_mutants(mutant):
     assert failed >= 1
 
 
+# ---- the two-layer chain with the column-parallel product ----------------
+
+def test_two_layer_chain_finite_differences():
+    pins.check_two_layer_finite_differences(_fwd, oracle.pcr_bwd, oracle.colpar_fwd, oracle.colpar_bwd)
+
+
+def test_two_layer_all_synced_is_vanilla():
+    pins.check_two_layer_all_synced_is_vanilla(_fwd, oracle.pcr_bwd, oracle.colpar_fwd, oracle.colpar_bwd)
+
+
+def test_two_layer_none_synced_is_ensemble():
+    pins.check_two_layer_none_synced_is_ensemble(_fwd, oracle.pcr_bwd, oracle.colpar_fwd, oracle.colpar_bwd)
+
+
+def _colbwd_allreduce(dU, A, W):
+    # the ordinary tensor-parallel backward: the input gradient summed over
+    # the ranks, as if every rank's input were the same tensor
+    dA, dW = oracle.colpar_bwd(dU, A, W)
+    return np.broadcast_to(dA.sum(axis=0), dA.shape).copy(), dW
+
+
+def _colbwd_next_rank_weight(dU, A, W):
+    dA, dW = oracle.colpar_bwd(dU, A, np.roll(np.asarray(W, dtype=np.float64), 1, axis=0))
+    return dA, oracle.colpar_bwd(dU, A, W)[1]
+
+
+def _colbwd_dw_from_wrong_rank(dU, A, W):
+    dA, _ = oracle.colpar_bwd(dU, A, W)
+    return dA, oracle.colpar_bwd(dU, np.roll(np.asarray(A, dtype=np.float64), 1, axis=0), W)[1]
+
+
+@pytest.mark.parametrize("mutant", [_colbwd_allreduce, _colbwd_next_rank_weight, _colbwd_dw_from_wrong_rank])
+def test_two_layer_pins_reject_mutants(mutant):
+    failed = 0
+    for chk in (pins.check_two_layer_finite_differences, pins.check_two_layer_all_synced_is_vanilla,
+                pins.check_two_layer_none_synced_is_ensemble):
+        try:
+            chk(_fwd, oracle.pcr_bwd, oracle.colpar_fwd, mutant)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin rejects {mutant.__name__}"
+    # the finite-difference pin alone catches every one of them
+    with pytest.raises(AssertionError):
+        pins.check_two_layer_finite_differences(_fwd, oracle.pcr_bwd, oracle.colpar_fwd, mutant)
+
+
 def test_golden_fixture_reproduces_from_oracle():
     """The stored fixture is exactly what the oracle writes today."""
     import json
