@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,colpar,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -97,7 +97,8 @@ def main():
     ops.lib()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep"}
+    legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
+                                                         "colpar"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -323,6 +324,25 @@ def main():
             torch.cuda.empty_cache()
         res["t_sweep"] = sweep
 
+    # ------------------------------------ column-parallel layer (per-rank input)
+    if "colpar" in legs:
+        # The Llama2-7B MLP up-projection as the column-parallel layer after
+        # a partial channel-reduce: rank t multiplies its own activation
+        # A_t [M, 4096] by its column slice [4096, 1376]; fwd + bwd.
+        Kc, Nc = H, KR
+        A = randn_bf16((T, M, Kc))
+        W1 = randn_bf16((T, Kc, Nc), 0.02)
+        dU = randn_bf16((T, M, Nc))
+        U = torch.empty((T, M, Nc), dtype=torch.bfloat16, device=dev)
+        dA, dW1 = torch.empty_like(A), torch.empty_like(W1)
+        tf = time_call(lambda: ops.colpar_fwd(A, W1, out=U), 10)
+        tb = time_call(lambda: ops.colpar_bwd(dU, A, W1, dA=dA, dW=dW1), 10)
+        fc = 2.0 * M * Kc * Nc * T
+        res["colpar_up_proj"] = {"K": Kc, "N_per_rank": Nc, "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+                                 "fwd_bwd_tflops": round(3 * fc / ((tf + tb) * 1e-3) / 1e12, 2)}
+        del A, W1, dU, U, dA, dW1
+        torch.cuda.empty_cache()
+
     # ------------------------------------------- copy of known size (counters)
     if "copy" in legs:
         # A plain streaming kernel of known size (1 GiB read, 1 GiB written;
@@ -374,6 +394,7 @@ def main():
         "reduce_only_f32": res.get("reduce_only_f32"),
         "reduce_only_bf16": res.get("reduce_only_bf16"),
         "t_sweep": res.get("t_sweep"),
+        "colpar_up_proj": res.get("colpar_up_proj"),
         "decode_down_proj": res.get("decode_down_proj"),
         "copy": res.get("copy"),
         "src": src_hash(),

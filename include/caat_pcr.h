@@ -102,6 +102,35 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
 size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H);
 
 /*
+ * Column-parallel linear layer with per-rank inputs: the layer that consumes
+ * the partial channel-reduce's output.  After the partial reduce the ranks'
+ * activations differ (paper, Introduction), so rank t multiplies its own
+ * activation A_t by its own column slice W_t of the next layer's weight:
+ *   A [T, M, K] bf16   rank t's activation (K = the hidden size)
+ *   W [T, K, N] bf16   rank t's column slice (N output columns per rank)
+ *   U [T, M, N] bf16   U[t] = A_t W_t   (fp32 accumulation, rounded once)
+ * Sizes and alignment as above with (Kr, H) = (K, N).  No workspace; U must
+ * not overlap A or W.
+ */
+int caat_colpar_fwd(const uint16_t* A, const uint16_t* W, uint16_t* U, int T, int M, int K, int N,
+                    void* stream);
+
+/*
+ * Backward of caat_colpar_fwd for per-rank incoming gradients dU[T,M,N]:
+ *   dA[t] = dU_t W_t^T   [M, K] bf16      dW[t] = A_t^T dU_t   [K, N] bf16
+ * (fp32 accumulation).  Each rank's input gradient stays on its rank: an
+ * ordinary tensor-parallel backward sums the column-parallel layer's input
+ * gradient over the ranks because that input is replicated, but here the
+ * inputs differ and the only cross-rank sum is the partial channel-reduce's
+ * own backward (caat_pcr_bwd with dZ = dA), over exactly the synced
+ * channels -- the forward/backward agreement the Introduction requires.
+ * dA or dW may be NULL to skip that product.  No workspace; outputs must not
+ * overlap the inputs or each other.
+ */
+int caat_colpar_bwd(const uint16_t* dU, const uint16_t* A, const uint16_t* W, uint16_t* dA, uint16_t* dW,
+                    int T, int M, int K, int N, void* stream);
+
+/*
  * The partial channel-reduce alone, on given per-rank activations Y[T,M,H]
  * of `dtype` (CAAT_F32 or CAAT_BF16):
  *   out[t][:, c] = Y[0][:, c] + Y[1][:, c] + ... + Y[T-1][:, c]   for c in S

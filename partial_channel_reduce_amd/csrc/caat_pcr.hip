@@ -132,15 +132,22 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
   return decode_counter_bytes(H) + round256((size_t)T * M * H * sizeof(float));
 }
 
-int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M,
-                        int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the row-parallel forward (mask = S) and the column-parallel
+// forward (mask == nullptr: nothing synced, no workspace used).
+int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr, int H,
+             void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_dims(T, M, Kr, H)) return st;
   // tensors with no elements (M == 0) may be passed as NULL
-  if (!W || !mask || (M > 0 && (!X || !out))) return CAAT_ERR_NULL;
+  if (!W || (M > 0 && (!X || !out))) return CAAT_ERR_NULL;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(out, 16) || !aligned(mask, 8)) return CAAT_ERR_ALIGN;
   const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nO = (size_t)T * M * H * 2;
-  if (M > 0 && (overlap(out, nO, X, nX) || overlap(out, nO, W, nW) || overlap(out, nO, mask, H))) return CAAT_ERR_ALIAS;
-  const size_t need = caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H);
+  if (M > 0 && (overlap(out, nO, X, nX) || overlap(out, nO, W, nW) || (mask && overlap(out, nO, mask, H))))
+    return CAAT_ERR_ALIAS;
+  const size_t need = mask ? caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return CAAT_ERR_WORKSPACE;
     if (overlap(workspace, need, out, nO) || overlap(workspace, need, X, nX) || overlap(workspace, need, W, nW) ||
@@ -148,11 +155,13 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
       return CAAT_ERR_ALIAS;
   }
   if (M == 0) return CAAT_OK;
+  if (!mask) workspace = nullptr;  // never touched without synced channels
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (use_decode(M, H)) {
     // workspace: the per-block arrival counters, then the fp32 partials
     int* arrivals = static_cast<int*>(workspace);
-    float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(H));
+    float* partial =
+        workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(H)) : nullptr;
     const dim3 grid(((H + kDecCols - 1) / kDecCols) * T);
     if (M <= 16)
       hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, arrivals,
@@ -166,21 +175,42 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
   return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
 }
 
+}  // namespace
+
+extern "C" {
+
+int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M,
+                        int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!mask) return CAAT_ERR_NULL;
+  return fwd_impl(X, W, mask, out, T, M, Kr, H, workspace, workspace_bytes, stream);
+}
+
+int caat_colpar_fwd(const uint16_t* A, const uint16_t* W, uint16_t* U, int T, int M, int K, int N, void* stream) {
+  return fwd_impl(A, W, nullptr, U, T, M, K, N, nullptr, 0, stream);
+}
+
 size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0) return 0;
   return round256((size_t)T * M * H * 2);  // G_t for every rank, bf16
 }
 
-int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* dX,
-                 uint16_t* dW, int T, int M, int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the row-parallel backward (mask = S: G = the partial
+// channel-reduce of dZ, materialised in the workspace) and the
+// column-parallel backward (mask == nullptr: G = dZ itself, no workspace).
+int bwd_impl(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* dX,
+             uint16_t* dW, int T, int M, int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_dims(T, M, Kr, H)) return st;
   // dZ and X have no elements when M == 0 and may then be NULL
-  if (!mask || (M > 0 && !dZ) || (dX && !W) || (M > 0 && dW && !X)) return CAAT_ERR_NULL;
+  if ((M > 0 && !dZ) || (dX && !W) || (M > 0 && dW && !X)) return CAAT_ERR_NULL;
   if (!aligned(dZ, 16) || (X && !aligned(X, 16)) || (W && !aligned(W, 16)) || (dX && !aligned(dX, 16)) ||
       (dW && !aligned(dW, 16)) || !aligned(mask, 8))
     return CAAT_ERR_ALIGN;
   const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nZ = (size_t)T * M * H * 2;
-  const void* ins[4] = {dZ, X, W, mask};
+  const void* ins[4] = {dZ, X, W, mask};  // a NULL entry is skipped
   const size_t nin[4] = {nZ, nX, nW, (size_t)H};
   for (int i = 0; i < 4; ++i) {
     if (!ins[i]) continue;
@@ -188,7 +218,7 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
     if (dW && overlap(dW, nW, ins[i], nin[i])) return CAAT_ERR_ALIAS;
   }
   if (dX && dW && overlap(dX, nX, dW, nW)) return CAAT_ERR_ALIAS;
-  const size_t need = caat_pcr_bwd_workspace_bytes(T, M, Kr, H);
+  const size_t need = mask ? caat_pcr_bwd_workspace_bytes(T, M, Kr, H) : 0;
   if (need > 0 && (dX || dW)) {
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return CAAT_ERR_WORKSPACE;
     for (int i = 0; i < 4; ++i)
@@ -206,9 +236,14 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
     }
     return CAAT_OK;
   }
-  // G_t = the partial channel-reduce of dZ, for every rank, into the workspace.
-  uint16_t* G = reinterpret_cast<uint16_t*>(workspace);
-  if (int st = launch_reduce_bf16(dZ, mask, G, T, M, H, s)) return st;
+  // G_t = the partial channel-reduce of dZ, for every rank, into the
+  // workspace; with nothing synced G is dZ.
+  const uint16_t* G = dZ;
+  if (mask) {
+    uint16_t* Gw = reinterpret_cast<uint16_t*>(workspace);
+    if (int st = launch_reduce_bf16(dZ, mask, Gw, T, M, H, s)) return st;
+    G = Gw;
+  }
   if (dX) {
     const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256, kBigTileWaves>(G, W, dX, T, M, Kr, H, s)
                                            : launch_dx<128, 128, 4>(G, W, dX, T, M, Kr, H, s);
@@ -220,6 +255,21 @@ int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const
     if (st) return st;
   }
   return CAAT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* dX,
+                 uint16_t* dW, int T, int M, int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!mask) return CAAT_ERR_NULL;
+  return bwd_impl(dZ, X, W, mask, dX, dW, T, M, Kr, H, workspace, workspace_bytes, stream);
+}
+
+int caat_colpar_bwd(const uint16_t* dU, const uint16_t* A, const uint16_t* W, uint16_t* dA, uint16_t* dW, int T,
+                    int M, int K, int N, void* stream) {
+  return bwd_impl(dU, A, W, nullptr, dA, dW, T, M, K, N, nullptr, 0, stream);
 }
 
 int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, int T, int M, int H, int dtype,

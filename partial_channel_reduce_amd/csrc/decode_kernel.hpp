@@ -179,7 +179,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   constexpr int NP = (RR + RPP - 1) / RPP;   // passes covering 16*NB rows
   const int q = tid % QPR, c4 = n0 + 4 * q, mt = tid / QPR;
   const bool inb = c4 < H;  // H is a multiple of 8, so all 4 channels are in range
-  const uint32_t mbits = inb ? *reinterpret_cast<const uint32_t*>(mask + c4) : 0u;
+  const uint32_t mbits = inb && mask != nullptr ? *reinterpret_cast<const uint32_t*>(mask + c4) : 0u;
   bool syn[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) syn[e] = ((mbits >> (8 * e)) & 0xffu) != 0;
@@ -201,7 +201,8 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
     *reinterpret_cast<u32x2*>(out + u * MH + (long long)m * H + c4) = pk;
   };
   // A channel block without synced channels (the same for all T workgroups
-  // of the block) needs no exchange: each rank writes its own values.
+  // of the block; every block when mask == nullptr) needs no exchange and
+  // no workspace: each rank writes its own values.
   if (!__syncthreads_or(mbits != 0u)) {
     if (inb)
 #pragma unroll

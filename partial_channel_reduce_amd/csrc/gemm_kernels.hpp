@@ -31,7 +31,9 @@ __device__ __forceinline__ int opaque(int v) {
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // ============================================================================
-// Forward.  One workgroup per (channel tile, token tile) walks the contraction
+// Forward.  (mask == nullptr: no channel is synced, i.e. T independent
+// products -- the column-parallel layer.)  One workgroup per (channel tile,
+// token tile) walks the contraction
 // of all T ranks in rank order.  Synced channels keep accumulating across the
 // rank boundaries, so their fp32 accumulator ends as the sum over ranks
 // (ascending t), formed once and written to every rank: bit-identical synced
@@ -82,7 +84,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int ch = chw + (lane >> 5) * 4 + i * 32 + q * 8;
-      const uint32_t m4 = ch < H ? *reinterpret_cast<const uint32_t*>(mask + ch) : 0u;
+      const uint32_t m4 = mask != nullptr && ch < H ? *reinterpret_cast<const uint32_t*>(mask + ch) : 0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) kb |= ((m4 >> (8 * r)) & 0xffu) ? (1u << (4 * q + r)) : 0u;
     }
@@ -179,7 +181,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
       if (tok < M && ch < H) st16_nt(ol + (long long)tok * H + ch, v);
     });
   }
-  if (T == 1) return;
+  if (T == 1 || mask == nullptr) return;  // nothing synced to hand to other ranks
   const int rows = min(S::WN, M - tkw);
   // Mask of this lane's drain chunk (8 channels).  When every chunk of the
   // wave is all-synced or all-local, synced chunks are written whole;

@@ -40,6 +40,8 @@ SIGNATURES = [
     ("caat_rowpar_pcr_fwd_workspace_bytes", _S, [_I, _I, _I, _I]),
     ("caat_pcr_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     ("caat_pcr_bwd_workspace_bytes", _S, [_I, _I, _I, _I]),
+    ("caat_colpar_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    ("caat_colpar_bwd", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     ("caat_partial_channel_reduce", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
 ]
 
@@ -196,3 +198,46 @@ def partial_channel_reduce(Y: torch.Tensor, mask: torch.Tensor, out: torch.Tenso
     st = lib().caat_partial_channel_reduce(_ptr(Y), _ptr(mask), _ptr(out), T, M, H, dt, _stream(dev))
     _check(st, "caat_partial_channel_reduce")
     return out
+
+
+def colpar_fwd(A: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """U[T,M,N] = A[t] @ W[t] for per-rank inputs A[T,M,K] (see caat_pcr.h)."""
+    _require(A, "A", torch.bfloat16, 3)
+    dev = A.device
+    _require(W, "W", torch.bfloat16, 3, dev)
+    T, M, K = A.shape
+    N = W.shape[2]
+    if W.shape[0] != T or W.shape[1] != K:
+        raise ValueError(f"shape mismatch: A{tuple(A.shape)} W{tuple(W.shape)}")
+    if out is None:
+        out = torch.empty((T, M, N), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != (T, M, N):
+        raise ValueError(f"out must be {(T, M, N)}, got {tuple(out.shape)}")
+    st = lib().caat_colpar_fwd(_ptr(A), _ptr(W), _ptr(out), T, M, K, N, _stream(dev))
+    _check(st, "caat_colpar_fwd")
+    return out
+
+
+def colpar_bwd(dU: torch.Tensor, A: torch.Tensor, W: torch.Tensor, dA: torch.Tensor | None = None,
+               dW: torch.Tensor | None = None, need_da: bool = True, need_dw: bool = True):
+    """(dA[T,M,K], dW[T,K,N]) for incoming per-rank gradients dU[T,M,N]."""
+    _require(dU, "dU", torch.bfloat16, 3)
+    dev = dU.device
+    _require(A, "A", torch.bfloat16, 3, dev)
+    _require(W, "W", torch.bfloat16, 3, dev)
+    T, M, N = dU.shape
+    K = A.shape[2]
+    if tuple(A.shape) != (T, M, K) or tuple(W.shape) != (T, K, N):
+        raise ValueError(f"shape mismatch: dU{tuple(dU.shape)} A{tuple(A.shape)} W{tuple(W.shape)}")
+    if need_da and dA is None:
+        dA = torch.empty((T, M, K), dtype=torch.bfloat16, device=dev)
+    if need_dw and dW is None:
+        dW = torch.empty((T, K, N), dtype=torch.bfloat16, device=dev)
+    if dA is not None:
+        _require(dA, "dA", torch.bfloat16, 3, dev)
+    if dW is not None:
+        _require(dW, "dW", torch.bfloat16, 3, dev)
+    st = lib().caat_colpar_bwd(_ptr(dU), _ptr(A), _ptr(W), _ptr(dA), _ptr(dW), T, M, K, N, _stream(dev))
+    _check(st, "caat_colpar_bwd")
+    return dA, dW

@@ -33,7 +33,8 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for n in ("caat_rowpar_pcr_fwd", "caat_pcr_bwd", "caat_partial_channel_reduce"):
+    for n in ("caat_rowpar_pcr_fwd", "caat_pcr_bwd", "caat_partial_channel_reduce", "caat_colpar_fwd",
+              "caat_colpar_bwd"):
         assert n in names
 
 
@@ -130,6 +131,36 @@ def test_bwd_validation(L):
     assert bwd(L, ws=A) == ALIAS  # workspace over dZ
     assert bwd(L, dX=None, dW=None) == OK  # nothing requested: nothing enqueued
     assert bwd(L, M=0, dW=None) == OK  # empty input, dX empty
+
+
+def colf(L, A_=A, W=B, U=D, T=4, M=64, K=64, N=64):
+    return L.caat_colpar_fwd(A_, W, U, T, M, K, N, None)
+
+
+def colb(L, dU=A, A_=B, W=C, dA=E, dW=E + (1 << 32), T=4, M=64, K=64, N=64):
+    return L.caat_colpar_bwd(dU, A_, W, dA, dW, T, M, K, N, None)
+
+
+def test_colpar_validation(L):
+    # host-side checks only: every call here returns before any launch
+    assert colf(L, A_=None) == NULL
+    assert colf(L, W=None) == NULL
+    assert colf(L, T=0) == DIM
+    assert colf(L, N=100) == DIM
+    assert colf(L, K=12) == DIM
+    assert colf(L, U=D + 2) == ALIGN
+    assert colf(L, U=A) == ALIAS  # U over A
+    assert colf(L, U=B + 16) == ALIAS  # U over W
+    assert colf(L, M=0) == OK  # empty: nothing enqueued
+    assert colb(L, dU=None) == NULL
+    assert colb(L, W=None) == NULL  # dA requested without W
+    assert colb(L, A_=None) == NULL  # dW requested without A
+    assert colb(L, N=12) == DIM
+    assert colb(L, dA=E + 4) == ALIGN
+    assert colb(L, dA=A) == ALIAS  # dA over dU
+    assert colb(L, dW=E) == ALIAS  # dW over dA
+    assert colb(L, dA=None, dW=None) == OK  # nothing requested
+    assert colb(L, M=0, dW=None) == OK  # empty input, dA empty
 
 
 def test_reduce_validation(L):
