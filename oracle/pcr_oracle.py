@@ -48,6 +48,7 @@ __all__ = [
     "pcr_bwd",
     "colpar_fwd",
     "colpar_bwd",
+    "residual_rmsnorm",
     "fwd_at",
     "bwd_dx_at",
     "bwd_dw_at",
@@ -145,6 +146,21 @@ def colpar_bwd(dU, A, W):
     dA = np.stack([dU[t] @ W[t].T for t in range(T)])
     dW = np.stack([A[t].T @ dU[t] for t in range(T)])
     return dA, dW
+
+
+def residual_rmsnorm(Z, R, gamma, eps: float):
+    """Per-rank residual update and RMS normalisation of the result.
+
+    The partial channel-reduce leaves each rank with its own activation Z[t]
+    (Introduction), which is added to that rank's own residual stream R[t];
+    the Llama-family blocks the pages train then RMS-normalise it:
+        Rn[t, m, :] = R[t, m, :] + Z[t, m, :]
+        N[t, m, :]  = Rn[t, m, :] / sqrt(mean_c Rn[t, m, c]**2 + eps) * gamma
+    -> (Rn, N), both [T,M,H]; gamma [H] is the same on every rank."""
+    Rn = bf16_to_f64(R) + bf16_to_f64(Z)
+    g = bf16_to_f64(gamma)
+    ms = np.mean(Rn * Rn, axis=-1, keepdims=True)
+    return Rn, Rn / np.sqrt(ms + eps) * g
 
 
 # ---------------------------------------------------------------------------

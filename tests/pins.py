@@ -301,3 +301,51 @@ def check_two_layer_none_synced_is_ensemble(fwd, bwd, colfwd, colbwd, seed=11):
         dX, _ = bwd(dZ, X, W, mask)
         want = np.matmul(np.matmul(C, np.transpose(W1, (0, 2, 1))), np.transpose(W, (0, 2, 1)))
         np.testing.assert_allclose(dX, want, rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# Residual update + RMS normalisation (the step after the partial reduce).
+# ---------------------------------------------------------------------------
+
+def check_rmsnorm_closed_forms(fn):
+    """Values the definition fixes by hand: x = (3, 4), eps = 1, gamma = 1
+    gives mean square 12.5 and x / sqrt(13.5); a one-hot row c*e_k with
+    eps = 0 gives sign(c) * sqrt(H) * gamma_k at k and zeros elsewhere; a
+    zero row with eps > 0 stays zero."""
+    Z = np.array([[[3.0, 4.0]]])
+    _, N = fn(Z, np.zeros_like(Z), np.ones(2), 1.0)
+    np.testing.assert_allclose(N[0, 0], [3.0 / np.sqrt(13.5), 4.0 / np.sqrt(13.5)], rtol=1e-14)
+    H = 16
+    gamma = np.linspace(0.5, 2.0, H)
+    for c, k in ((2.5, 3), (-7.0, 0), (0.125, 15)):
+        Z = np.zeros((1, 1, H))
+        Z[0, 0, k] = c
+        _, N = fn(Z, np.zeros_like(Z), gamma, 0.0)
+        want = np.zeros(H)
+        want[k] = np.sign(c) * np.sqrt(H) * gamma[k]
+        np.testing.assert_allclose(N[0, 0], want, rtol=1e-13, atol=1e-15)
+    _, N = fn(np.zeros((2, 3, 8)), np.zeros((2, 3, 8)), np.ones(8), 1e-5)
+    assert np.all(N == 0.0)
+
+
+def check_rmsnorm_invariants(fn, seed=12):
+    """The residual update is the plain sum; with eps = 0 the norm is
+    invariant to positive scaling of a row, odd in the row, and with
+    gamma = 1 every output row has mean square 1 and points along R + Z."""
+    rng = np.random.default_rng(seed)
+    T, M, H = 3, 5, 24
+    Z = rng.standard_normal((T, M, H))
+    R = rng.standard_normal((T, M, H))
+    g = rng.uniform(0.5, 1.5, H)
+    Rn, N = fn(Z, R, g, 0.0)
+    np.testing.assert_allclose(Rn, Z + R, rtol=0, atol=0)
+    _, N2 = fn(3.5 * Z, 3.5 * R, g, 0.0)
+    np.testing.assert_allclose(N2, N, rtol=1e-13, atol=1e-14)
+    _, N3 = fn(-Z, -R, g, 0.0)
+    np.testing.assert_allclose(N3, -N, rtol=1e-13, atol=1e-14)
+    _, N1 = fn(Z, R, np.ones(H), 0.0)
+    np.testing.assert_allclose(np.mean(N1 * N1, axis=-1), 1.0, rtol=1e-13)
+    # what is normalised is the updated residual R + Z: with gamma = 1 each
+    # output row is that sum divided by its root mean square
+    S = Z + R
+    np.testing.assert_allclose(N1 * np.sqrt(np.mean(S * S, axis=-1, keepdims=True)), S, rtol=1e-12, atol=1e-13)

@@ -276,6 +276,48 @@ def test_two_layer_pins_reject_mutants(mutant):
         pins.check_two_layer_finite_differences(_fwd, oracle.pcr_bwd, oracle.colpar_fwd, mutant)
 
 
+# ---- residual update + RMS normalisation ---------------------------------
+
+def test_rmsnorm_closed_forms():
+    pins.check_rmsnorm_closed_forms(oracle.residual_rmsnorm)
+
+
+def test_rmsnorm_invariants():
+    pins.check_rmsnorm_invariants(oracle.residual_rmsnorm)
+
+
+def _rms_sum_not_mean(Z, R, g, eps):
+    Rn = np.asarray(Z, np.float64) + np.asarray(R, np.float64)
+    return Rn, Rn / np.sqrt(np.sum(Rn * Rn, axis=-1, keepdims=True) + eps) * np.asarray(g, np.float64)
+
+
+def _rms_eps_outside(Z, R, g, eps):
+    Rn = np.asarray(Z, np.float64) + np.asarray(R, np.float64)
+    return Rn, Rn / (np.sqrt(np.mean(Rn * Rn, axis=-1, keepdims=True)) + eps) * np.asarray(g, np.float64)
+
+
+def _rms_no_gamma(Z, R, g, eps):
+    Rn = np.asarray(Z, np.float64) + np.asarray(R, np.float64)
+    return Rn, Rn / np.sqrt(np.mean(Rn * Rn, axis=-1, keepdims=True) + eps)
+
+
+def _rms_norm_before_residual(Z, R, g, eps):
+    Z = np.asarray(Z, np.float64)
+    Rn = Z + np.asarray(R, np.float64)
+    return Rn, Z / np.sqrt(np.mean(Z * Z, axis=-1, keepdims=True) + eps) * np.asarray(g, np.float64)
+
+
+@pytest.mark.parametrize("mutant", [_rms_sum_not_mean, _rms_eps_outside, _rms_no_gamma, _rms_norm_before_residual])
+def test_rmsnorm_pins_reject_mutants(mutant):
+    failed = 0
+    for chk in (pins.check_rmsnorm_closed_forms, pins.check_rmsnorm_invariants):
+        try:
+            chk(mutant)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin rejects {mutant.__name__}"
+
+
 def test_golden_fixture_reproduces_from_oracle():
     """The stored fixture is exactly what the oracle writes today."""
     import json
