@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,colpar,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,colpar,norm,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -98,7 +98,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar"}
+                                                         "colpar", "norm"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -343,6 +343,22 @@ def main():
         del A, W1, dU, U, dA, dW1
         torch.cuda.empty_cache()
 
+    # ------------------------------- residual update + RMS norm (per rank)
+    if "norm" in legs:
+        # The step after the partial reduce at the Llama2-7B shape: each rank
+        # adds its activation to its residual stream and RMS-normalises it;
+        # reads Z and R, writes the new residual and the normalised rows.
+        Zn = randn_bf16((T, M, H))
+        Rn = randn_bf16((T, M, H))
+        gn = (1.0 + 0.1 * torch.randn((H,), generator=gen, device=dev)).to(torch.bfloat16)
+        ro, no = torch.empty_like(Zn), torch.empty_like(Zn)
+        t = time_call(lambda: ops.residual_rmsnorm(Zn, Rn, gn, 1e-5, r_out=ro, n_out=no), 10)
+        nbytes = 4.0 * T * M * H * 2
+        gbs = nbytes / (t * 1e-3) / 1e9
+        res["residual_rmsnorm"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del Zn, Rn, gn, ro, no
+        torch.cuda.empty_cache()
+
     # ------------------------------------------- copy of known size (counters)
     if "copy" in legs:
         # A plain streaming kernel of known size (1 GiB read, 1 GiB written;
@@ -395,6 +411,7 @@ def main():
         "reduce_only_bf16": res.get("reduce_only_bf16"),
         "t_sweep": res.get("t_sweep"),
         "colpar_up_proj": res.get("colpar_up_proj"),
+        "residual_rmsnorm": res.get("residual_rmsnorm"),
         "decode_down_proj": res.get("decode_down_proj"),
         "copy": res.get("copy"),
         "src": src_hash(),

@@ -131,6 +131,23 @@ int caat_colpar_bwd(const uint16_t* dU, const uint16_t* A, const uint16_t* W, ui
                     int T, int M, int K, int N, void* stream);
 
 /*
+ * The step after the partial channel-reduce in the Llama-family blocks the
+ * paper trains (reproducibility table: Llama2-7B, TinyLlama-1.1B): each rank
+ * adds its own activation Z_t -- rank-specific after the partial reduce
+ * (Introduction) -- to its own residual stream R_t and RMS-normalises the
+ * result with the norm weight gamma (the same on every rank):
+ *   Rout[t,m,:] = bf16(R[t,m,:] + Z[t,m,:])
+ *   N[t,m,:]    = bf16(Rn * gamma / sqrt(mean_c Rn^2 + eps)),  Rn = the rounded Rout row
+ * in fp32; the row's sum of squares is formed in a fixed order, so results
+ * are bitwise reproducible.  Z, R, Rout, N [T,M,H] bf16; gamma [H] bf16;
+ * 0 <= eps (finite).  H <= 8192.  Rout == R updates the residual stream in
+ * place; otherwise Rout must not overlap Z, R or gamma.  N must not overlap
+ * any other argument.  No workspace.
+ */
+int caat_residual_rmsnorm(const uint16_t* Z, const uint16_t* R, const uint16_t* gamma, uint16_t* Rout,
+                          uint16_t* N, int T, int M, int H, float eps, void* stream);
+
+/*
  * The partial channel-reduce alone, on given per-rank activations Y[T,M,H]
  * of `dtype` (CAAT_F32 or CAAT_BF16):
  *   out[t][:, c] = Y[0][:, c] + Y[1][:, c] + ... + Y[T-1][:, c]   for c in S

@@ -6,6 +6,7 @@
 
 #include "decode_kernel.hpp"
 #include "gemm_kernels.hpp"
+#include "norm_kernels.hpp"
 #include "reduce_kernels.hpp"
 
 namespace {
@@ -305,6 +306,35 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
   } else {
     return launch_reduce_bf16(static_cast<const uint16_t*>(Y), mask, static_cast<uint16_t*>(out), T, M, H, s);
   }
+  return launched();
+}
+
+int caat_residual_rmsnorm(const uint16_t* Z, const uint16_t* R, const uint16_t* gamma, uint16_t* Rout, uint16_t* N,
+                          int T, int M, int H, float eps, void* stream) {
+  if (T < 1 || T > kMaxT || M < 0 || H < 8 || H % 8 != 0 || H > 8 * kNormThreads * kNormMaxVecs) return CAAT_ERR_DIM;
+  if ((long long)T * M >= (1LL << 31)) return CAAT_ERR_DIM;
+  if (!(eps >= 0.0f) || eps > 1e30f) return CAAT_ERR_DIM;  // also rejects NaN
+  if (!gamma || (M > 0 && (!Z || !R || !Rout || !N))) return CAAT_ERR_NULL;
+  if (!aligned(Z, 16) || !aligned(R, 16) || !aligned(gamma, 16) || !aligned(Rout, 16) || !aligned(N, 16))
+    return CAAT_ERR_ALIGN;
+  const size_t n = (size_t)T * M * H * 2, ng = (size_t)H * 2;
+  if (M > 0) {
+    if (Rout != R && (overlap(Rout, n, R, n) || overlap(Rout, n, Z, n) || overlap(Rout, n, gamma, ng)))
+      return CAAT_ERR_ALIAS;
+    if (Rout == R && (overlap(R, n, Z, n) || overlap(R, n, gamma, ng))) return CAAT_ERR_ALIAS;
+    if (overlap(N, n, Z, n) || overlap(N, n, R, n) || overlap(N, n, Rout, n) || overlap(N, n, gamma, ng))
+      return CAAT_ERR_ALIAS;
+  }
+  if (M == 0) return CAAT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((long long)T * M));
+  const int hv = H / 8;
+  if (hv <= kNormThreads)
+    hipLaunchKernelGGL(pcr_residual_rmsnorm_kernel<1>, grid, dim3(kNormThreads), 0, s, Z, R, gamma, Rout, N, H, eps);
+  else if (hv <= 2 * kNormThreads)
+    hipLaunchKernelGGL(pcr_residual_rmsnorm_kernel<2>, grid, dim3(kNormThreads), 0, s, Z, R, gamma, Rout, N, H, eps);
+  else
+    hipLaunchKernelGGL(pcr_residual_rmsnorm_kernel<4>, grid, dim3(kNormThreads), 0, s, Z, R, gamma, Rout, N, H, eps);
   return launched();
 }
 

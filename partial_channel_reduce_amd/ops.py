@@ -42,6 +42,7 @@ SIGNATURES = [
     ("caat_pcr_bwd_workspace_bytes", _S, [_I, _I, _I, _I]),
     ("caat_colpar_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     ("caat_colpar_bwd", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    ("caat_residual_rmsnorm", _I, [_P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
     ("caat_partial_channel_reduce", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
 ]
 
@@ -241,3 +242,30 @@ def colpar_bwd(dU: torch.Tensor, A: torch.Tensor, W: torch.Tensor, dA: torch.Ten
     st = lib().caat_colpar_bwd(_ptr(dU), _ptr(A), _ptr(W), _ptr(dA), _ptr(dW), T, M, K, N, _stream(dev))
     _check(st, "caat_colpar_bwd")
     return dA, dW
+
+
+def residual_rmsnorm(Z: torch.Tensor, R: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
+                     r_out: torch.Tensor | None = None, n_out: torch.Tensor | None = None, inplace: bool = False):
+    """(Rn, N): per-rank residual update Rn = R + Z and its RMS normalisation
+    (see caat_pcr.h).  inplace=True writes Rn into R."""
+    _require(Z, "Z", torch.bfloat16, 3)
+    dev = Z.device
+    _require(R, "R", torch.bfloat16, 3, dev)
+    _require(gamma, "gamma", torch.bfloat16, 1, dev)
+    T, M, H = Z.shape
+    if tuple(R.shape) != (T, M, H) or gamma.shape[0] != H:
+        raise ValueError(f"shape mismatch: Z{tuple(Z.shape)} R{tuple(R.shape)} gamma{tuple(gamma.shape)}")
+    if inplace:
+        r_out = R
+    elif r_out is None:
+        r_out = torch.empty_like(Z)
+    if n_out is None:
+        n_out = torch.empty_like(Z)
+    _require(r_out, "r_out", torch.bfloat16, 3, dev)
+    _require(n_out, "n_out", torch.bfloat16, 3, dev)
+    if tuple(r_out.shape) != (T, M, H) or tuple(n_out.shape) != (T, M, H):
+        raise ValueError("outputs must have Z's shape")
+    st = lib().caat_residual_rmsnorm(_ptr(Z), _ptr(R), _ptr(gamma), _ptr(r_out), _ptr(n_out), T, M, H, float(eps),
+                                     _stream(dev))
+    _check(st, "caat_residual_rmsnorm")
+    return r_out, n_out

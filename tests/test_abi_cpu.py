@@ -163,6 +163,30 @@ def test_colpar_validation(L):
     assert colb(L, M=0, dW=None) == OK  # empty input, dA empty
 
 
+def rms(L, Z=A, R=B, g=C, Ro=D, N=E, T=4, M=64, H=64, eps=1e-5):
+    return L.caat_residual_rmsnorm(Z, R, g, Ro, N, T, M, H, eps, None)
+
+
+def test_residual_rmsnorm_validation(L):
+    # host-side checks only: every call here returns before any launch
+    assert rms(L, Z=None) == NULL
+    assert rms(L, g=None) == NULL
+    assert rms(L, N=None) == NULL
+    assert rms(L, H=100) == DIM
+    assert rms(L, H=8200) == DIM  # above 8192 channels
+    assert rms(L, T=0) == DIM
+    assert rms(L, eps=-1.0) == DIM
+    assert rms(L, eps=float("nan")) == DIM
+    assert rms(L, Ro=D + 2) == ALIGN
+    assert rms(L, g=C + 8) == ALIGN
+    assert rms(L, Ro=A) == ALIAS  # Rout over Z
+    assert rms(L, Ro=B + 16) == ALIAS  # Rout partly over R (not in place)
+    assert rms(L, N=B) == ALIAS  # N over R
+    assert rms(L, N=D) == ALIAS  # N over Rout
+    assert rms(L, R=A, Ro=A) == ALIAS  # in-place update of a residual that overlaps Z
+    assert rms(L, M=0) == OK  # empty: nothing enqueued
+
+
 def test_reduce_validation(L):
     red = L.caat_partial_channel_reduce
     assert red(None, C, D, 8, 16, 64, 0, None) == NULL
