@@ -299,6 +299,29 @@ def main():
         res["decode_down_proj"] = dec
         del Ws
         torch.cuda.empty_cache()
+        # the attention out-projection (Kr = 512): 33.6 MB of weights; 16 sets
+        # rotate (537 MB, beyond the last-level cache)
+        deco = {}
+        nso = 16
+        Wo = [randn_bf16((T, KR_OUT, H), 0.02) for _ in range(nso)]
+        for Md in DEC_M:
+            Xo = [randn_bf16((T, Md, KR_OUT)) for _ in range(nso)]
+            oo = [torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev) for _ in range(nso)]
+            wso = torch.zeros(max(1, ops.fwd_workspace_bytes(T, Md, KR_OUT, H)), dtype=torch.uint8, device=dev)
+            idx = [0]
+
+            def callo():
+                i = idx[0] % nso
+                idx[0] += 1
+                ops.rowpar_pcr_fwd(Xo[i], Wo[i], mk, out=oo[i], workspace=wso)
+
+            t = time_call(callo, 64, warm=16)
+            nbytes = 2.0 * (T * Md * KR_OUT + T * KR_OUT * H + T * Md * H)
+            gbs = nbytes / (t * 1e-3) / 1e9
+            deco[f"M{Md}"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        res["decode_out_proj"] = deco
+        del Wo
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------ tensor-parallel sweep
     if "tsweep" in legs:
@@ -413,6 +436,7 @@ def main():
         "colpar_up_proj": res.get("colpar_up_proj"),
         "residual_rmsnorm": res.get("residual_rmsnorm"),
         "decode_down_proj": res.get("decode_down_proj"),
+        "decode_out_proj": res.get("decode_out_proj"),
         "copy": res.get("copy"),
         "src": src_hash(),
     }
