@@ -72,9 +72,9 @@ const char* caat_status_string(int status);
  *   out[t][:, c] = sum_u Y_u[:, c]     for c in S   (same value on every rank)
  *   out[t][:, c] = Y_t[:, c]           for c not in S
  * rounded once to bf16 (nearest even).  `out` must not overlap X, W or mask.
- * Decode-shaped calls (M <= 32) run a weight-streaming kernel that needs
- * caat_rowpar_pcr_fwd_workspace_bytes() bytes of workspace; other M need none
- * (pass NULL, 0).  The workspace starts with ceil(H/128) 32-bit arrival
+ * Decode-shaped calls (M <= 192, taken 32 tokens at a time) run a
+ * weight-streaming kernel that needs caat_rowpar_pcr_fwd_workspace_bytes()
+ * bytes of workspace; other M need none (pass NULL, 0).  The workspace starts with ceil(H/128) 32-bit arrival
  * counters (padded to 256 bytes) that must be zero when a call starts; every
  * call leaves them zero again, so zero a new workspace once before its first
  * use.  The rest (fp32 partials of the synced channels) may hold anything.

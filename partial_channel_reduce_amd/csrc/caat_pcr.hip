@@ -123,16 +123,21 @@ const char* caat_status_string(int status) {
   }
 }
 
-// Decode-shaped calls: a few tokens, and one rank's fp32 partials [M][H]
+// Decode-shaped calls: up to kDecChunkedMaxM tokens, taken 32 at a time by
+// the weight-streaming kernel (each chunk reads the weights once more; up
+// to six chunks that still beats the tiled kernel, which has too few tiles
+// to fill the chip at these sizes), and one chunk's fp32 partials [32][H]
 // addressable with 32-bit byte offsets.
-static bool use_decode(int M, int H) { return M > 0 && M <= kDecMaxM && (size_t)M * H * 4 < ((size_t)1 << 31); }
+static bool use_decode(int M, int H) {
+  return M > 0 && M <= kDecChunkedMaxM && (size_t)kDecMaxM * H * 4 < ((size_t)1 << 31);
+}
 
 // Arrival counters of the decode kernel: one int per channel block.
 static size_t decode_counter_bytes(int H) { return round256((size_t)((H + kDecCols - 1) / kDecCols) * sizeof(int)); }
 
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || !use_decode(M, H)) return 0;
-  return decode_counter_bytes(H) + round256((size_t)T * M * H * sizeof(float));
+  return decode_counter_bytes(H) + round256((size_t)T * (M < kDecMaxM ? M : kDecMaxM) * H * sizeof(float));
 }
 
 }  // extern "C"
@@ -166,13 +171,22 @@ int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t
     float* partial =
         workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(H)) : nullptr;
     const dim3 grid(((H + kDecCols - 1) / kDecCols) * T);
-    if (M <= 16)
-      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, arrivals,
-                         T, M, Kr, H);
-    else
-      hipLaunchKernelGGL(rowpar_pcr_decode_kernel<2>, grid, dim3(kDecThreads), 0, s, X, W, mask, out, partial, arrivals,
-                         T, M, Kr, H);
-    return launched();
+    const long long xs = (long long)M * Kr, os = (long long)M * H;  // rank strides of X and out
+    // Chunks run one after another on the stream and share the workspace;
+    // each launch leaves the arrival counters at zero for the next.
+    for (int m0 = 0; m0 < M; m0 += kDecMaxM) {
+      const int mc = M - m0 < kDecMaxM ? M - m0 : kDecMaxM;
+      const uint16_t* Xc = X + (long long)m0 * Kr;
+      uint16_t* oc = out + (long long)m0 * H;
+      if (mc <= 16)
+        hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc, partial,
+                           arrivals, T, mc, Kr, H, xs, os);
+      else
+        hipLaunchKernelGGL(rowpar_pcr_decode_kernel<2>, grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc, partial,
+                           arrivals, T, mc, Kr, H, xs, os);
+      if (int st = launched()) return st;
+    }
+    return CAAT_OK;
   }
   if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s);
   return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);

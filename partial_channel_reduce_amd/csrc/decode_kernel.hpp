@@ -25,7 +25,8 @@
 
 namespace caat {
 
-constexpr int kDecMaxM = 32;     // two 16-row MFMA blocks
+constexpr int kDecMaxM = 32;     // two 16-row MFMA blocks per launch
+constexpr int kDecChunkedMaxM = 192;  // larger M up to this: one launch per 32-token chunk
 constexpr int kDecCols = 128;    // channels per workgroup: 256 bytes of each weight row
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
@@ -44,12 +45,16 @@ __device__ __forceinline__ int dec_off(int k, int ch) {
   return k * kDecCols + (((ch >> 3) ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 3) + (ch & 7);
 }
 
-template <int NB>  // MFMA row blocks of 16 tokens: 1 (M <= 16) or 2
+// NB: MFMA row blocks of 16 tokens, 1 (M <= 16) or 2.  The M token rows of
+// rank t start at X + t * xs and out + t * os (xs = M * Kr and os = M * H
+// for a whole call; larger when the call is one 32-token chunk of a bigger
+// batch, X and out then pointing at the chunk's first row).
+template <int NB>
 __global__ void __launch_bounds__(kDecThreads)
 rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                          float* __restrict__ partial, int* __restrict__ arrivals, int T, int M, int Kr,
-                         int H) {
+                         int H, long long xs, long long os) {
   constexpr int D = 2;                      // stages held in registers: one being used, one loading
   constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
   constexpr int SLOT = SE;                  // one LDS slot per wave
@@ -79,7 +84,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // past Kr read as zero (out of the buffer's range).
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + t * KH, (uint32_t)(KH * 2));
   const uint32_t xbytes = (uint32_t)(MK * 2);
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X + t * MK, xbytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X + t * xs, xbytes);
   const int wr = lane / kDecLpr, wc = lane % kDecLpr;
   const int wvoff = (wr * H + wc * 8) * 2;
   const int xr = lane & 15, xc = lane >> 4;  // A-fragment layout: token row, 8-k chunk
@@ -198,7 +203,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
     u32x2 pk;
     pk[0] = pack_bf16x2(v[0], v[1]);
     pk[1] = pack_bf16x2(v[2], v[3]);
-    *reinterpret_cast<u32x2*>(out + u * MH + (long long)m * H + c4) = pk;
+    *reinterpret_cast<u32x2*>(out + u * os + (long long)m * H + c4) = pk;
   };
   // A channel block without synced channels (the same for all T workgroups
   // of the block; every block when mask == nullptr) needs no exchange and

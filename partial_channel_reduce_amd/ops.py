@@ -120,7 +120,7 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """out[T,M,H] = partial channel-reduce of X[t] @ W[t] (see caat_pcr.h).
 
-    A caller-supplied `workspace` for decode-shaped calls (M <= 32) must be
+    A caller-supplied `workspace` for decode-shaped calls (M <= 192) must be
     zeroed once before its first use; the library leaves its counters zero."""
     _require(X, "X", torch.bfloat16, 3)
     dev = X.device

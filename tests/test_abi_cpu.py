@@ -103,10 +103,13 @@ def test_fwd_validation(L):
 
 def test_workspace_sizes(L):
     T, Kr, H = 8, 1376, 4096
-    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 33, Kr, H) == 0  # tiled path needs none
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 193, Kr, H) == 0  # tiled path needs none
     for M in (1, 8, 32):
         need = L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H)
         assert need >= 256 + T * M * H * 4 and need % 256 == 0  # arrival counters + fp32 partials
+    # 33 .. 192 tokens run 32 at a time and share one chunk's partials
+    for M in (33, 100, 192):
+        assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == L.caat_rowpar_pcr_fwd_workspace_bytes(T, 32, Kr, H)
     assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) >= T * 16384 * H * 2  # G for every rank
     assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) % 256 == 0
     assert L.caat_pcr_bwd_workspace_bytes(T, 0, Kr, H) == 0

@@ -152,6 +152,10 @@ INT_CASES = [
     (4, 5, 64, 200, "prefix", 0.0),      # decode, nothing synced (no exchange), ragged block
     (4, 9, 64, 200, "prefix", 1.0),      # decode, everything synced, ragged block
     (13, 20, 40, 392, "prefix", 0.5),    # decode, T = 13, one mixed block between uniform ones
+    (8, 33, 1376, 512, "random", 0.5),   # decode in 32-token chunks: 32 + 1
+    (8, 100, 96, 264, "prefix", 0.5),    # chunks 32 + 32 + 32 + 4
+    (13, 70, 40, 136, "random", 0.5),    # chunks, T = 13
+    (4, 192, 64, 200, "strided", 0.5),   # the largest chunked M
 ]
 
 
@@ -194,6 +198,8 @@ RAND_CASES = [
     (8, 8, 1376, 4096, "random", 0.5),
     (8, 32, 1376, 4096, "random", 0.5),
     (8, 32, 512, 4096, "random", 0.5),
+    (8, 64, 1376, 4096, "random", 0.5),   # two decode chunks
+    (8, 192, 512, 4096, "random", 0.5),   # six decode chunks
 ]
 
 
