@@ -43,6 +43,7 @@ RAND_CASES = [
     (8, 1, 4096, 1376),   # decode, Llama2-7B up-projection shape
     (8, 32, 4096, 1376),  # decode, two token blocks
     (5, 7, 72, 40),       # decode, ragged
+    (8, 64, 4096, 1376),  # decode in two 32-token chunks
     (1, 70, 64, 128),     # T = 1
 ]
 
@@ -69,6 +70,7 @@ def test_colpar_random_parity(ops, T, M, K, N):
 INT_CASES = [
     (4, 300, 72, 136),      # tiled path, ragged
     (8, 8, 1376, 520),      # decode
+    (8, 100, 1376, 520),    # decode in 32-token chunks
     (2, 16424, 40, 2056),   # 256x256 forward tiles (585 of them)
     (3, 16424, 520, 72),    # 256x256 input-gradient tiles
     (3, 200, 1288, 8456),   # 256x256 weight-gradient tiles
