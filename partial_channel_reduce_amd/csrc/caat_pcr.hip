@@ -189,6 +189,9 @@ int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t
     return CAAT_OK;
   }
   if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s);
+  // Fewer than 256 tiles of 128 x 128: 64-token tiles give twice as many
+  // workgroups (each walks all T ranks, so the tile count is what fills the chip).
+  if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 256) return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
   return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
 }
 

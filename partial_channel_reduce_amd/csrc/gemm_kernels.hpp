@@ -57,9 +57,9 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   using S = TileShape<BM, BN, NW>;
   using RS = RowStage<S::WM>;
   constexpr int REG = S::BUF / NW;             // boundary staging per wave (elements)
-  constexpr int PASSES = S::WM * S::WN / REG;  // boundary passes over the wave's sub-tile
-  constexpr int JPP = S::WJ / PASSES;          // 32-token blocks per pass
-  static_assert(PASSES * REG == S::WM * S::WN && JPP * PASSES == S::WJ, "staging split");
+  constexpr int PASSES = (S::WM * S::WN + REG - 1) / REG;  // boundary passes over the wave's sub-tile
+  constexpr int JPP = S::WJ / PASSES;                      // 32-token blocks per pass
+  static_assert(PASSES * REG >= S::WM * S::WN && JPP * PASSES == S::WJ && JPP * 32 * S::WM <= REG, "staging split");
   static_assert(NW * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
