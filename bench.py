@@ -34,6 +34,8 @@ T, M, KR, H, P = 8, 16384, 1376, 4096, 0.5
 KR_OUT = 512
 DEC_M = (1, 8, 32)
 COPY_ELEMS = 1 << 28           # fp32 elements of the calibration kernel (1 GiB each way)
+PAYLOAD_P = (0.25, 0.5, 0.75, 1.0)  # sync fractions of the payload leg (prefix masks)
+PAYLOAD_CALLS = 3                   # in-place reduce calls per p before its timing
 COPY_KERNEL_KEY = "neg_kernel"  # substring naming torch's elementwise negation kernel
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_7b_down_proj.txt")
 
@@ -49,11 +51,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,colpar,norm,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,colpar,norm,payload,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
                          "--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 csv run of the train leg, and exit")
+    ap.add_argument("--rocprof-payload", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the in-place reduce's calibrated bytes per dispatch for each p of the payload leg "
+                         "from two rocprofv3 --pmc csv runs of `--only payload,copy`, and exit")
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
                          "calibrated against the copy leg's kernel, and exit")
@@ -77,6 +82,9 @@ def main():
     if args.rocprof_mfma:
         print(rocprof_mfma_summary(args.rocprof_mfma))
         return
+    if args.rocprof_payload:
+        print(rocprof_payload_summary(*args.rocprof_payload))
+        return
     if args.rocprof_traffic:
         print(rocprof_traffic_summary(*args.rocprof_traffic))
         return
@@ -98,7 +106,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar", "norm"}
+                                                         "colpar", "norm", "payload"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -392,6 +400,26 @@ def main():
         del Zn, Rn, gn, ro, no
         torch.cuda.empty_cache()
 
+    # ------------------------------------ payload of the in-place reduce vs p
+    if "payload" in legs:
+        # In place with S = the first p*H channels, the reduce touches only
+        # the synced channels: its traffic should scale with p (the payload
+        # cut the pages claim for the partial reduce).  PAYLOAD_CALLS calls
+        # per p, in the order of PAYLOAD_P (the counter summary relies on it).
+        pay = {}
+        Yp = torch.randn((T, 4096, H), generator=gen, device=dev, dtype=torch.float32)
+        for pp in PAYLOAD_P:
+            mkp = torch.from_numpy(synth.make_mask(H, pp, "prefix")).to(dev)
+            for _ in range(PAYLOAD_CALLS):
+                ops.partial_channel_reduce(Yp, mkp, inplace=True)
+            torch.cuda.synchronize()
+            t = time_call(lambda: ops.partial_channel_reduce(Yp, mkp, inplace=True), 5, warm=0)
+            pay[f"p{pp}"] = {"us": round(t * 1e3, 2),
+                             "GB/s_synced": round(2.0 * T * 4096 * H * 4 * pp / (t * 1e-3) / 1e9, 1)}
+        res["payload_inplace_reduce"] = pay
+        del Yp
+        torch.cuda.empty_cache()
+
     # ------------------------------------------- copy of known size (counters)
     if "copy" in legs:
         # A plain streaming kernel of known size (1 GiB read, 1 GiB written;
@@ -447,6 +475,7 @@ def main():
         "residual_rmsnorm": res.get("residual_rmsnorm"),
         "decode_down_proj": res.get("decode_down_proj"),
         "decode_out_proj": res.get("decode_out_proj"),
+        "payload_inplace_reduce": res.get("payload_inplace_reduce"),
         "copy": res.get("copy"),
         "src": src_hash(),
     }
@@ -518,6 +547,40 @@ def rocprof_mfma_summary(d: str) -> str:
             continue
         fl = sum(mops) / len(mops) * 512
         out.append(f"| {_short(k)} | {len(util)} | {sum(util) / len(util):.1f} | {fl / 1e9:.1f} | {fl / algo:.3f} |")
+    return "\n".join(out)
+
+
+def rocprof_payload_summary(fetch_dir: str, write_dir: str) -> str:
+    """Bytes per dispatch of the in-place fp32 reduce for each p of the payload
+    leg (dispatches in order, PAYLOAD_CALLS + 5 per p, see the leg), scaled
+    by what the counters read for the calibration kernel."""
+    def series(d, counter):
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv")) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0))))
+        red = [float(r["Counter_Value"]) for r in rows if "pcr_reduce_f32_kernel" in r["Kernel_Name"]]
+        cal = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL_KEY in r["Kernel_Name"]]
+        return red, sum(cal) / len(cal)
+
+    fr, fc = series(fetch_dir, "FETCH_SIZE")
+    wr, wc = series(write_dir, "WRITE_SIZE")
+    known_kib = COPY_ELEMS * 4 / 1024.0
+    sf, sw = known_kib / fc, known_kib / wc
+    per = PAYLOAD_CALLS + 5  # dispatches per p: the untimed calls, then 5 timed ones (no warm-up)
+    if len(fr) != per * len(PAYLOAD_P) or len(wr) != len(fr):
+        raise SystemExit(f"unexpected reduce dispatch count {len(fr)} / {len(wr)}")
+    full = 2.0 * T * 4096 * H * 4  # out-of-place bytes of the whole tensor
+    out = [f"scale: FETCH_SIZE x{sf:.4f}, WRITE_SIZE x{sw:.4f} (calibration kernel, {COPY_ELEMS * 4} bytes each way)", "",
+           "| p | HBM read MB | HBM write MB | total MB | / total at p = 1 | synced bytes 2*T*M*H*4*p, MB |",
+           "|---|---|---|---|---|---|"]
+    tot = {}
+    for i, pp in enumerate(PAYLOAD_P):
+        f = sum(fr[i * per:(i + 1) * per]) / per * sf * 1024
+        w = sum(wr[i * per:(i + 1) * per]) / per * sw * 1024
+        tot[pp] = (f, w)
+    t1 = sum(tot[1.0])
+    for pp in PAYLOAD_P:
+        f, w = tot[pp]
+        out.append(f"| {pp} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} | {(f + w) / t1:.3f} | {full * pp / 1e6:.1f} |")
     return "\n".join(out)
 
 
