@@ -32,7 +32,6 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 T, M, KR, H, P = 8, 16384, 1376, 4096, 0.5
 KR_OUT = 512
-DEC_M = (1, 8, 32)
 COPY_ELEMS = 1 << 28           # fp32 elements of the calibration kernel (1 GiB each way)
 PAYLOAD_P = (0.25, 0.5, 0.75, 1.0)  # sync fractions of the payload leg (prefix masks)
 PAYLOAD_CALLS = 3                   # in-place reduce calls per p before its timing
@@ -51,7 +50,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,tsweep,colpar,norm,payload,copy (profiling runs)")
+    ap.add_argument("--reduce-m", default="16384,4096,1,8,32",
+                    help="token counts of the reduce leg (<= 32: latency points; counter runs take one at a time)")
+    ap.add_argument("--decode-m", default="1,8,32", help="token counts of the decode legs (counter runs take one at a time)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,decode_out,tsweep,colpar,norm,payload,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -106,7 +108,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar", "norm", "payload"}
+                                                         "colpar", "norm", "payload", "decode_out"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -259,7 +261,8 @@ def main():
     if "reduce" in legs:
         red = {}
         mk = mask_dev(H, seed=1)
-        for Mr in (16384, 4096):
+        red_m = [int(x) for x in args.reduce_m.split(",") if x]
+        for Mr in [m for m in red_m if m > 32]:
             Y = torch.randn((T, Mr, H), generator=gen, device=dev, dtype=torch.float32)
             o = torch.empty_like(Y)
             t = time_call(lambda: ops.partial_channel_reduce(Y, mk, out=o), 10)
@@ -268,7 +271,7 @@ def main():
             red[f"M{Mr}"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
             del Y, o
         # decode-sized reduces: latency-bound, rotate 64 buffer sets (> the 256 MB last-level cache)
-        for Mr in DEC_M:
+        for Mr in [m for m in red_m if m <= 32]:
             sets = [torch.randn((T, Mr, H), generator=gen, device=dev) for _ in range(64)]
             outs = [torch.empty_like(x) for x in sets]
             idx = [0]
@@ -299,7 +302,8 @@ def main():
         mk = mask_dev(H)
         nsets = 6  # 6 x 90 MB of weights: beyond the 256 MB last-level cache
         Ws = [randn_bf16((T, KR, H), 0.02) for _ in range(nsets)]
-        for Md in DEC_M:
+        dec_m = [int(x) for x in args.decode_m.split(",") if x]
+        for Md in dec_m:
             Xs = [randn_bf16((T, Md, KR)) for _ in range(nsets)]
             outs = [torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
             wsd = torch.zeros(max(1, ops.fwd_workspace_bytes(T, Md, KR, H)), dtype=torch.uint8, device=dev)
@@ -317,12 +321,16 @@ def main():
         res["decode_down_proj"] = dec
         del Ws
         torch.cuda.empty_cache()
+
+    if "decode_out" in legs:
         # the attention out-projection (Kr = 512): 33.6 MB of weights; 16 sets
         # rotate (537 MB, beyond the last-level cache)
+        mk = mask_dev(H)
+        dec_m = [int(x) for x in args.decode_m.split(",") if x]
         deco = {}
         nso = 16
         Wo = [randn_bf16((T, KR_OUT, H), 0.02) for _ in range(nso)]
-        for Md in DEC_M:
+        for Md in dec_m:
             Xo = [randn_bf16((T, Md, KR_OUT)) for _ in range(nso)]
             oo = [torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev) for _ in range(nso)]
             wso = torch.zeros(max(1, ops.fwd_workspace_bytes(T, Md, KR_OUT, H)), dtype=torch.uint8, device=dev)
