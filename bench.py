@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--rocprof-payload", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the in-place reduce's calibrated bytes per dispatch for each p of the payload leg "
                          "from two rocprofv3 --pmc csv runs of `--only payload,copy`, and exit")
+    ap.add_argument("--rocprof-stall", nargs=3, metavar=("SQ_DIR", "TCP_DIR", "TA_DIR"),
+                    help="print where the GEMMs' memory path waits (L1 stalls on L2 data, TA/TD busy, L2 hit rate, "
+                         "LDS bank conflicts, wave waits) from three rocprofv3 --pmc csv runs of the train leg, and exit")
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
                          "calibrated against the copy leg's kernel, and exit")
@@ -86,6 +89,9 @@ def main():
         return
     if args.rocprof_payload:
         print(rocprof_payload_summary(*args.rocprof_payload))
+        return
+    if args.rocprof_stall:
+        print(rocprof_stall_summary(*args.rocprof_stall))
         return
     if args.rocprof_traffic:
         print(rocprof_traffic_summary(*args.rocprof_traffic))
@@ -555,6 +561,46 @@ def rocprof_mfma_summary(d: str) -> str:
             continue
         fl = sum(mops) / len(mops) * 512
         out.append(f"| {_short(k)} | {len(util)} | {sum(util) / len(util):.1f} | {fl / 1e9:.1f} | {fl / algo:.3f} |")
+    return "\n".join(out)
+
+
+STALL_PASSES = (
+    ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS",
+     "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+    ("TCP_PENDING_STALL_CYCLES_sum", "TCP_TCP_TA_DATA_STALL_CYCLES_sum", "TCP_TCR_TCP_STALL_CYCLES_sum",
+     "TCP_READ_TAGCONFLICT_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE"),
+    ("TA_TA_BUSY_sum", "TA_BUFFER_READ_LDS_WAVEFRONTS_sum", "TD_TD_BUSY_sum", "TCC_HIT_sum", "TCC_MISS_sum",
+     "TCC_TAG_STALL_sum", "GRBM_GUI_ACTIVE"),
+)
+
+
+def rocprof_stall_summary(*dirs: str) -> str:
+    """Where the products' copy path waits, from three counter passes
+    (STALL_PASSES, one per directory).  GRBM_GUI_ACTIVE sums the 8 XCDs'
+    active cycles, so one XCD's = GUI / 8; per-CU units (TCP, TA, TD, LDS) are
+    normalised by 256 x that, SIMD-wide ones by 1024 x that."""
+    per = []
+    for d in dirs:
+        acc = {}
+        for r in _read_csv(_find(d, "counter_collection.csv")):
+            acc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        per.append({k: sum(v) / len(v) for k, v in acc.items()})
+    kernels = sorted({k for k, _ in per[0]} & {k for k, _ in per[1]} & {k for k, _ in per[2]})
+    kernels = [k for k in kernels if any(s in k for s in ("pcr_fwd", "pcr_bwd", "pcr_reduce"))]
+    out = ["| kernel | MFMA busy | L1 stalled on L2 data | TA busy | TD busy | L2 hit rate | "
+           "LDS bank-conflict cycles | wave cycles waiting (any / for issue) |",
+           "|---|---|---|---|---|---|---|---|"]
+    for k in kernels:
+        g = lambda i, c: per[i].get((k, c), float("nan"))
+        cyc = [g(i, "GRBM_GUI_ACTIVE") / 8 for i in range(3)]
+        hit, miss = g(2, "TCC_HIT_sum"), g(2, "TCC_MISS_sum")
+        wc = g(0, "SQ_WAVE_CYCLES")
+        out.append(
+            f"| {_short(k)} | {g(0, 'SQ_VALU_MFMA_BUSY_CYCLES') / (cyc[0] * 1024):.2f} "
+            f"| {g(1, 'TCP_PENDING_STALL_CYCLES_sum') / (cyc[1] * 256):.2f} "
+            f"| {g(2, 'TA_TA_BUSY_sum') / (cyc[2] * 256):.2f} | {g(2, 'TD_TD_BUSY_sum') / (cyc[2] * 256):.2f} "
+            f"| {hit / (hit + miss):.3f} | {g(0, 'SQ_LDS_BANK_CONFLICT') / (cyc[0] * 256):.4f} "
+            f"| {g(0, 'SQ_WAIT_ANY') / wc:.2f} / {g(0, 'SQ_WAIT_INST_ANY') / wc:.2f} |")
     return "\n".join(out)
 
 
