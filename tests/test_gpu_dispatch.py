@@ -1,0 +1,97 @@
+"""GPU parity on both sides of every kernel-selection threshold.
+
+The library picks a kernel by problem size: the weight-streaming decode
+kernel up to 192 tokens, then GEMM tiles of 128x64, 128x128 or 256x256 by
+how many tiles the output has (fewer than the chip's 256 CUs take the
+smaller tiles).  Each case here sits one token or eight channels below or
+above such a switch, so an off-by-one in the selection or in a kernel's
+edge handling shows up as a wrong element.  Integer-valued inputs keep every
+product and sum exact in bf16 and fp32, so the comparison with the oracle is
+bitwise."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from partial_channel_reduce_amd import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from partial_channel_reduce_amd import ops as _ops
+
+    _ops.lib()
+    return _ops
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _int_grad(T, M, H, seed, nz=0.3):
+    rng = np.random.default_rng(seed)
+    dZ = rng.integers(-1, 2, size=(T, M, H)) * (rng.random((T, M, H)) < nz)
+    return synth.f32_to_bf16_bits(dZ.astype(np.float32))
+
+
+def _tiles(rows, cols, tr, tc, batch=1):
+    return -(-rows // tr) * -(-cols // tc) * batch
+
+
+# Forward, H = 1024 channels (8 tiles of 128, 4 of 256):
+#   M <= 192 decode;  M = 193 the first 128x64-tile call;
+#   M = 3968 -> 248 tiles of 128x128 (still 128x64), M = 3969 -> 256 (128x128);
+#   M = 16128 -> 252 tiles of 256x256 (still 128x128), M = 16129 -> 256 (256x256).
+FWD_M = [192, 193, 3968, 3969, 16128, 16129]
+
+
+@pytest.mark.parametrize("M", FWD_M)
+def test_fwd_across_kernel_switch(ops, M):
+    T, Kr, H = 2, 40, 1024
+    assert _tiles(3968, H, 128, 128) == 248 and _tiles(3969, H, 128, 128) == 256
+    assert _tiles(16128, H, 256, 256) == 252 and _tiles(16129, H, 256, 256) == 256
+    _announce(f"dispatch fwd T={T} M={M} Kr={Kr} H={H}")
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=M, lo=-1, hi=1, x_zero_frac=0.4)
+    mask = synth.make_mask(H, 0.5, "random", seed=M + 1)
+    ref = oracle.rowpar_pcr_fwd(X, W, mask)
+    assert np.abs(ref).max() <= 256
+    out = ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(out), ref)
+
+
+# dX = G W^T, T = 4, Kr = 520 (3 row tiles of 256): M = 5376 -> 21 token tiles,
+# 252 big tiles (128x128 kernel); M = 5377 -> 22, 264 big tiles (256x256).
+@pytest.mark.parametrize("M", [5376, 5377])
+def test_dx_across_kernel_switch(ops, M):
+    T, Kr, H = 4, 520, 72
+    assert _tiles(M, Kr, 256, 256, T) == (252 if M == 5376 else 264)
+    _announce(f"dispatch dX T={T} M={M} Kr={Kr} H={H}")
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=M, lo=-1, hi=1, x_zero_frac=0.5)
+    dZ = _int_grad(T, M, H, M)
+    mask = synth.make_mask(H, 0.5, "random", seed=M + 2)
+    rdX, _ = oracle.pcr_bwd(dZ, X, W, mask)
+    assert np.abs(rdX).max() <= 256
+    dXd, _ = ops.pcr_bwd(G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), need_dw=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(dXd), rdX)
+
+
+# dW = X^T G, T = 4, Kr = 264 (2 row tiles of 256): H = 7936 -> 31 channel
+# tiles, 248 big tiles (128x128 kernel); H = 7944 -> 32, 256 (256x256).
+@pytest.mark.parametrize("H", [7936, 7944])
+def test_dw_across_kernel_switch(ops, H):
+    T, M, Kr = 4, 40, 264
+    assert _tiles(Kr, H, 256, 256, T) == (248 if H == 7936 else 256)
+    _announce(f"dispatch dW T={T} M={M} Kr={Kr} H={H}")
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=H, lo=-1, hi=1, x_zero_frac=0.5)
+    dZ = _int_grad(T, M, H, H)
+    mask = synth.make_mask(H, 0.5, "random", seed=H + 3)
+    _, rdW = oracle.pcr_bwd(dZ, X, W, mask)
+    assert np.abs(rdW).max() <= 256
+    _, dWd = ops.pcr_bwd(G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), need_dx=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(dWd), rdW)
