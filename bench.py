@@ -32,6 +32,16 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 T, M, KR, H, P = 8, 16384, 1376, 4096, 0.5
 KR_OUT = 512
+# The smaller models' row-parallel layers (name, T, M, Kr, H, mask kind), all at p = 0.5:
+# the 130M model (h = 768, 8 x 1024 tokens) and TinyLlama-1.1B (h = 2048, 16 x 2048 tokens).
+MODEL_SHAPES = (
+    ("130M down-proj", 8, 8192, 384, 768, "random"),
+    ("130M out-proj", 8, 8192, 96, 768, "random"),
+    ("1.1B down-proj", 8, 32768, 704, 2048, "prefix"),
+    ("1.1B down-proj", 8, 32768, 704, 2048, "strided"),
+    ("1.1B out-proj", 8, 32768, 256, 2048, "prefix"),
+    ("1.1B out-proj", 8, 32768, 256, 2048, "strided"),
+)
 COPY_ELEMS = 1 << 28           # fp32 elements of the calibration kernel (1 GiB each way)
 PAYLOAD_P = (0.25, 0.5, 0.75, 1.0)  # sync fractions of the payload leg (prefix masks)
 PAYLOAD_CALLS = 3                   # in-place reduce calls per p before its timing
@@ -53,7 +63,7 @@ def parse():
     ap.add_argument("--reduce-m", default="16384,4096,1,8,32",
                     help="token counts of the reduce leg (<= 32: latency points; counter runs take one at a time)")
     ap.add_argument("--decode-m", default="1,8,32", help="token counts of the decode legs (counter runs take one at a time)")
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,reduce,decode,decode_out,tsweep,colpar,norm,payload,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,shapes,reduce,decode,decode_out,tsweep,colpar,norm,payload,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -114,7 +124,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar", "norm", "payload", "decode_out"}
+                                                         "colpar", "norm", "payload", "decode_out", "shapes"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -262,6 +272,58 @@ def main():
         }
         del Xo, Wo, dZo, outo, dXo, dWo, wso
         torch.cuda.empty_cache()
+
+    # -------------------------------------------- the smaller models' layers
+    if "shapes" in legs:
+        # Forward and backward of each layer against its roofline: algorithmic
+        # flops 2*M*(T*Kr)*H (backward twice that) and bytes X + W + out
+        # (backward dZ + X + W read, dX + dW written); the bound is the
+        # larger of flops / bf16 peak and bytes / HBM peak.  Buffer sets are
+        # rotated so that every call streams at least 600 MB: operands do not
+        # sit in the 256 MB last-level cache between calls.
+        rows = []
+        for name, Ts, Ms, Ks, Hs, kind in MODEL_SHAPES:
+            bf = 2 * (Ts * Ms * Ks + Ts * Ks * Hs + Ts * Ms * Hs)
+            bb = 2 * (Ts * Ms * Hs + 2 * Ts * Ms * Ks + 2 * Ts * Ks * Hs)
+            nset = max(1, min(4, -(-600_000_000 // bf)))
+            sets = []
+            for _ in range(nset):
+                sets.append((randn_bf16((Ts, Ms, Ks)), randn_bf16((Ts, Ks, Hs), 0.02), randn_bf16((Ts, Ms, Hs)),
+                             torch.empty((Ts, Ms, Hs), dtype=torch.bfloat16, device=dev),
+                             torch.empty((Ts, Ms, Ks), dtype=torch.bfloat16, device=dev),
+                             torch.empty((Ts, Ks, Hs), dtype=torch.bfloat16, device=dev)))
+            mks = mask_dev(Hs, kind=kind)
+            wss = torch.empty(ops.bwd_workspace_bytes(Ts, Ms, Ks, Hs), dtype=torch.uint8, device=dev)
+            ctr = [0]
+
+            def fwd_call():
+                Xs, Ws, _, Os, _, _ = sets[ctr[0] % nset]
+                ctr[0] += 1
+                ops.rowpar_pcr_fwd(Xs, Ws, mks, out=Os)
+
+            def bwd_call():
+                Xs, Ws, dZs, _, dXs, dWs = sets[ctr[0] % nset]
+                ctr[0] += 1
+                ops.pcr_bwd(dZs, Xs, Ws, mks, dX=dXs, dW=dWs, workspace=wss)
+
+            iters = 4 * nset
+            tf = time_call(fwd_call, iters, warm=nset)
+            tb = time_call(bwd_call, iters, warm=nset)
+            ff = 2.0 * Ms * (Ts * Ks) * Hs
+            roof_f = max(ff / (PEAK_BF16_TFLOPS * 1e9), bf / (PEAK_HBM_GBS * 1e6))  # ms
+            roof_b = max(2 * ff / (PEAK_BF16_TFLOPS * 1e9), bb / (PEAK_HBM_GBS * 1e6))
+            rows.append({
+                "layer": name, "T": Ts, "M": Ms, "Kr": Ks, "H": Hs, "mask": kind, "p": P,
+                "fwd_us": round(tf * 1e3, 1), "bwd_us": round(tb * 1e3, 1),
+                "fwd_bound": "mfma" if ff / bf > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm",
+                "fwd_tflops": round(ff / (tf * 1e-3) / 1e12, 1), "fwd_GBs": round(bf / (tf * 1e-3) / 1e9, 1),
+                "fwd_frac_roof": round(roof_f / tf, 3),
+                "bwd_tflops": round(2 * ff / (tb * 1e-3) / 1e12, 1), "bwd_frac_roof": round(roof_b / tb, 3),
+            })
+            log(f"{name} ({kind}): fwd {tf * 1e3:.1f} us ({roof_f / tf:.2f} of roofline), bwd {tb * 1e3:.1f} us")
+            del sets, mks, wss
+            torch.cuda.empty_cache()
+        res["model_shapes"] = rows
 
     # ------------------------------------------------------ reduce-only fp32
     if "reduce" in legs:
@@ -482,6 +544,7 @@ def main():
         "prefix_mask": res.get("prefix_mask"),
         "library_gemm": res.get("library_gemm"),
         "out_proj": res.get("out_proj"),
+        "model_shapes": res.get("model_shapes"),
         "reduce_only_f32": res.get("reduce_only_f32"),
         "reduce_only_bf16": res.get("reduce_only_bf16"),
         "t_sweep": res.get("t_sweep"),

@@ -189,9 +189,13 @@ int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t
     return CAAT_OK;
   }
   if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s);
-  // Fewer than 256 tiles of 128 x 128: 64-token tiles give twice as many
-  // workgroups (each walks all T ranks, so the tile count is what fills the chip).
-  if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 256) return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
+  // Fewer than 512 tiles of 128 x 128 (two per CU): 64-token tiles give
+  // twice as many workgroups (each walks all T ranks, so the tile count is
+  // what fills the chip), up to three resident per CU.  Measured with the
+  // same bits: 130M down-proj (384 tiles) 100 -> 91 us, out-proj 74 -> 68 us,
+  // 7B down-proj at M = 1024 (256 tiles) 179 -> 154 us; at 512-1023 tiles the
+  // 64-token tiles lose (M = 2048: 243 -> 321 us).
+  if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 512) return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
   return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
 }
 

@@ -2,7 +2,7 @@
 
 The library picks a kernel by problem size: the weight-streaming decode
 kernel up to 192 tokens, then GEMM tiles of 128x64, 128x128 or 256x256 by
-how many tiles the output has (fewer than the chip's 256 CUs take the
+how many tiles the output has (too few to fill the chip's 256 CUs take the
 smaller tiles).  Each case here sits one token or eight channels below or
 above such a switch, so an off-by-one in the selection or in a kernel's
 edge handling shows up as a wrong element.  Integer-valued inputs keep every
@@ -43,15 +43,15 @@ def _tiles(rows, cols, tr, tc, batch=1):
 
 # Forward, H = 1024 channels (8 tiles of 128, 4 of 256):
 #   M <= 192 decode;  M = 193 the first 128x64-tile call;
-#   M = 3968 -> 248 tiles of 128x128 (still 128x64), M = 3969 -> 256 (128x128);
+#   M = 8064 -> 504 tiles of 128x128 (still 128x64), M = 8065 -> 512 (128x128);
 #   M = 16128 -> 252 tiles of 256x256 (still 128x128), M = 16129 -> 256 (256x256).
-FWD_M = [192, 193, 3968, 3969, 16128, 16129]
+FWD_M = [192, 193, 8064, 8065, 16128, 16129]
 
 
 @pytest.mark.parametrize("M", FWD_M)
 def test_fwd_across_kernel_switch(ops, M):
     T, Kr, H = 2, 40, 1024
-    assert _tiles(3968, H, 128, 128) == 248 and _tiles(3969, H, 128, 128) == 256
+    assert _tiles(8064, H, 128, 128) == 504 and _tiles(8065, H, 128, 128) == 512
     assert _tiles(16128, H, 256, 256) == 252 and _tiles(16129, H, 256, 256) == 256
     _announce(f"dispatch fwd T={T} M={M} Kr={Kr} H={H}")
     X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=M, lo=-1, hi=1, x_zero_frac=0.4)
