@@ -92,8 +92,12 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  *   dX[t] = G_t W_t^T   [M, Kr] bf16      dW[t] = X_t^T G_t   [Kr, H] bf16
  * G's synced channels are rounded to bf16 once (they feed bf16 MFMA); both
  * products accumulate in fp32.  dX or dW may be NULL to skip that product.
- * Needs caat_pcr_bwd_workspace_bytes() = T*M*H*2 bytes (rounded up to 256)
- * of workspace, any contents on entry; on return it holds G[T,M,H] (bf16).
+ * Needs caat_pcr_bwd_workspace_bytes() bytes of workspace, any contents on
+ * entry: T*M*H*2 (rounded up to 256) for G[T,M,H] (bf16), which it holds on
+ * return, plus, when dW has fewer 128x128 tiles than the chip has CUs and
+ * M spans at least 16 chunks of 64 tokens, s*T*Kr*H*4 bytes after it for
+ * dW's fp32 sums over s pieces of the token range (added in piece order, so
+ * the result does not depend on scheduling).
  * Outputs must not overlap the inputs, the workspace or each other.
  */
 int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask,

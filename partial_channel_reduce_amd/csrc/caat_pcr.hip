@@ -43,6 +43,14 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // MFMAs; the 128x128 tiles of small problems keep four.
 constexpr int kBigTileWaves = 8;
 
+// 256 x 256 tiles (eight waves) when there are at least as many as CUs,
+// else 128 x 128 (four waves).  (At 256 to 511 big tiles, e.g. the weight
+// gradient of a 512-row out-projection shard, one big tile per CU beats four
+// small ones: 0.64 -> 0.50 ms.)
+bool use_big_tiles(long long rows, long long cols, long long batch) {
+  return ((rows + 255) / 256) * ((cols + 255) / 256) * batch >= 256;
+}
+
 template <int BM, int BN, int NW>
 int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
                int H, hipStream_t s) {
@@ -64,7 +72,46 @@ template <int BM, int BN, int NW>
 int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, hipStream_t s) {
   const int tm = (H + BM - 1) / BM, tn = (Kr + BN - 1) / BN;  // channel tiles x dW row tiles
   hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN, NW>), dim3(T * tm * tn), dim3(NW * 64), 0, s, G, X, dW, T, M, Kr,
-                     H, tm, tn);
+                     H, tm, tn, nullptr, 1, (M + kBK - 1) / kBK);
+  return launched();
+}
+
+// Split of dW's token range: with fewer 128 x 128 tiles than CUs (and no
+// 256 x 256 tiling), dW_t = X_t^T G_t is cut into pieces of at least eight
+// 64-token chunks so that about 256 workgroups run; returns the number of
+// pieces (1: no split) and the chunks per piece.
+struct DwSplit {
+  int splits, kcs;
+};
+DwSplit dw_split(int T, int M, int Kr, int H) {
+  const int nkm = (M + kBK - 1) / kBK;
+  DwSplit d{1, nkm};
+  if (M <= 0 || use_big_tiles(Kr, H, T)) return d;
+  const long long tiles = (long long)((H + 127) / 128) * ((Kr + 127) / 128) * T;
+  if (tiles >= 256) return d;
+  int sp = (int)((256 + tiles - 1) / tiles);
+  if (sp > nkm / 8) sp = nkm / 8;
+  if (sp < 2) return d;
+  d.kcs = (nkm + sp - 1) / sp;
+  d.splits = (nkm + d.kcs - 1) / d.kcs;  // every piece has at least one chunk
+  return d;
+}
+
+size_t dw_split_bytes(int T, int M, int Kr, int H) {
+  const DwSplit d = dw_split(T, M, Kr, H);
+  return d.splits > 1 ? (size_t)d.splits * T * Kr * H * sizeof(float) : 0;
+}
+
+// dW through fp32 pieces in `part` (dw_split_bytes of them), then their sum.
+int launch_dw_split(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, float* part,
+                    const DwSplit& d, hipStream_t s) {
+  const int tm = (H + 127) / 128, tn = (Kr + 127) / 128;
+  hipLaunchKernelGGL((pcr_bwd_dw_kernel<128, 128, 4, true>), dim3(T * d.splits * tm * tn), dim3(256), 0, s, G, X,
+                     dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs);
+  if (int st = launched()) return st;
+  const long long n4 = (long long)T * Kr * H / 4;
+  hipLaunchKernelGGL(dw_split_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, part, dW, d.splits,
+                     n4);
   return launched();
 }
 
@@ -95,13 +142,6 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
   return launched();
 }
 
-// 256 x 256 tiles (eight waves) when there are at least as many as CUs,
-// else 128 x 128 (four waves).  (At 256 to 511 big tiles, e.g. the weight
-// gradient of a 512-row out-projection shard, one big tile per CU beats four
-// small ones: 0.64 -> 0.50 ms.)
-bool use_big_tiles(long long rows, long long cols, long long batch) {
-  return ((rows + 255) / 256) * ((cols + 255) / 256) * batch >= 256;
-}
 
 }  // namespace
 
@@ -215,7 +255,8 @@ int caat_colpar_fwd(const uint16_t* A, const uint16_t* W, uint16_t* U, int T, in
 
 size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0) return 0;
-  return round256((size_t)T * M * H * 2);  // G_t for every rank, bf16
+  // G_t for every rank (bf16), then dW's fp32 token-range pieces when dW is split
+  return round256((size_t)T * M * H * 2) + dw_split_bytes(T, M, Kr, H);
 }
 
 }  // extern "C"
@@ -274,8 +315,15 @@ int bwd_impl(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uin
     if (st) return st;
   }
   if (dW) {
-    const int st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256, kBigTileWaves>(G, X, dW, T, M, Kr, H, s)
-                                           : launch_dw<128, 128, 4>(G, X, dW, T, M, Kr, H, s);
+    const DwSplit d = dw_split(T, M, Kr, H);
+    int st;
+    if (mask && d.splits > 1)  // the pieces live in the workspace, after G
+      st = launch_dw_split(G, X, dW, T, M, Kr, H,
+                           reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)T * M * H * 2)),
+                           d, s);
+    else
+      st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256, kBigTileWaves>(G, X, dW, T, M, Kr, H, s)
+                                   : launch_dw<128, 128, 4>(G, X, dW, T, M, Kr, H, s);
     if (st) return st;
   }
   return CAAT_OK;

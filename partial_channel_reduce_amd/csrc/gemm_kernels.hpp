@@ -318,10 +318,16 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W
 // are MNCONT: A = G_t ([m][c]), B = X_t ([m][k]).  Token rows past M read as
 // zero (outside the rank's buffer).
 // ============================================================================
-template <int BM, int BN, int NW>
+//
+// SPLIT: when dW_t has too few tiles to fill the chip, the token range is cut
+// into `splits` pieces of `kcs` chunks; workgroup (t, piece, tile) leaves its
+// fp32 sum over its piece in part[piece][t][k][c], and dw_split_sum_kernel
+// adds the pieces in order and rounds once.
+template <int BM, int BN, int NW, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64, 1)
 pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X, uint16_t* __restrict__ dW,
-                  int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
+                  int T, int M, int Kr, int H, int tiles_m, int tiles_n, float* __restrict__ part, int splits,
+                  int kcs) {
   using S = TileShape<BM, BN, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -332,12 +338,16 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
   const int wm = wave % S::WGM, wn = wave / S::WGM;
   const int per_rank = tiles_m * tiles_n;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = lin / per_rank;
+  const int t = lin / (splits * per_rank);
+  const int rest = lin - t * splits * per_rank;
+  const int piece = rest / per_rank;
   int tm, tn;
-  tile_coords(lin - t * per_rank, tiles_m, tiles_n, tm, tn);
+  tile_coords(rest - piece * per_rank, tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, k0r = tn * BN;  // channels (dW columns), rows of dW
   const long long MH = (long long)M * H, MK = (long long)M * Kr;
-  const int nk = (M + kBK - 1) / kBK;
+  const int nkm = (M + kBK - 1) / kBK;
+  const int cb = piece * kcs;                       // this piece's chunks: cb .. ce-1
+  const int ce = cb + kcs < nkm ? cb + kcs : nkm;
 
   f32x16 acc[S::WI][S::WJ];
   zero_acc<BM, BN, NW>(acc);
@@ -353,8 +363,8 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
   // A wave whose rows of dW_t all lie past Kr (the last row tile when Kr is
   // not a multiple of BN) only issues its share of the copies.
   auto loop = [&](auto compute) {
-    issue(0);
-    for (int c = 0; c < nk; ++c) {
+    issue(cb);
+    for (int c = cb; c < ce; ++c) {
       uint16_t* As = smem + (c & 1) * S::BUF;
       uint16_t* Bs = As + BM * kBK;
       __builtin_amdgcn_s_waitcnt(0);
@@ -363,9 +373,9 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
         mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
                           [&](int ks, int j) { return frag_mncont<BN>(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                           [&] {
-                            if (c + 1 < nk) issue(c + 1);
+                            if (c + 1 < ce) issue(c + 1);
                           });
-      else if (c + 1 < nk)
+      else if (c + 1 < ce)
         issue(c + 1);
     }
   };
@@ -373,6 +383,29 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
     loop(std::true_type{});
   else
     loop(std::false_type{});
+
+  const int cw = c0 + wm * S::WM, kw = k0r + wn * S::WN;
+  if constexpr (SPLIT) {
+    // fp32 piece sums straight from the accumulators: register group q of
+    // block (i, j) holds channels cw + 32i + 8q + 4(lane/32) .. +3 of dW row
+    // kw + 32j + lane%32 (16 contiguous bytes).
+    float* pt = part + ((long long)piece * T + t) * Kr * H;
+#pragma unroll
+    for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+      for (int j = 0; j < S::WJ; ++j) {
+        const int k = kw + j * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cw + i * 32 + q * 8 + (lane >> 5) * 4;
+          if (k < Kr && c < H) {
+            f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(pt + (long long)k * H + c) = v;
+          }
+        }
+      }
+    return;
+  }
 
   // Stage the transposed sub-tile through LDS and write whole rows of dW_t.
   using RS = RowStage<S::WM>;
@@ -387,11 +420,25 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
     }
   lds_wave_sync();
   uint16_t* dWt = dW + (long long)t * Kr * H;
-  const int cw = c0 + wm * S::WM, kw = k0r + wn * S::WN;
   RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
     const int k = kw + r, c = cw + cc * 8;
     if (k < Kr && c < H) st16(dWt + (long long)k * H + c, v);
   });
+}
+
+// dW = the sum of the pieces' fp32 partials in piece order, rounded once to
+// bf16: four consecutive elements per thread (n4 = T*Kr*H/4 groups).
+__global__ void dw_split_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ dW, int splits,
+                                    long long n4) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(part) + i;
+  f32x4 v = p[0];
+  for (int s = 1; s < splits; ++s) v += p[(long long)s * n4];
+  u32x2 o;
+  o[0] = pack_bf16x2(v[0], v[1]);
+  o[1] = pack_bf16x2(v[2], v[3]);
+  reinterpret_cast<u32x2*>(dW)[i] = o;
 }
 
 }  // namespace caat

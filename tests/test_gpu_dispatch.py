@@ -95,3 +95,41 @@ def test_dw_across_kernel_switch(ops, H):
     _, dWd = ops.pcr_bwd(G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), need_dx=False)
     torch.cuda.synchronize()
     assert np.array_equal(G.from_dev_bf16(dWd), rdW)
+
+
+# dW with too few tiles to fill the chip runs as a split of the token range:
+# fp32 pieces summed in piece order.  T = 2, Kr = 96, H = 264: six 128x128
+# tiles, M = 4000 tokens (62.5 chunks of 64) -> seven pieces of nine chunks,
+# the last one ragged.
+def test_dw_split_token_range_bitexact(ops):
+    T, M, Kr, H = 2, 4000, 96, 264
+    _announce(f"dW split T={T} M={M} Kr={Kr} H={H}")
+    base = -(-(T * M * H * 2) // 256) * 256
+    assert ops.bwd_workspace_bytes(T, M, Kr, H) - base == 7 * T * Kr * H * 4
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=77, lo=-1, hi=1, x_zero_frac=0.8)
+    dZ = _int_grad(T, M, H, 77, nz=0.2)
+    mask = synth.make_mask(H, 0.5, "random", seed=77)
+    rdX, rdW = oracle.pcr_bwd(dZ, X, W, mask)
+    assert np.abs(rdW).max() <= 256 and np.abs(rdX).max() <= 256
+    args = (G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
+    dXd, dWd = ops.pcr_bwd(*args)
+    dXe, dWe = ops.pcr_bwd(*args)  # a second call: same bits
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(dWd), rdW)
+    assert np.array_equal(G.from_dev_bf16(dXd), rdX)
+    assert torch.equal(dWd.view(torch.int16), dWe.view(torch.int16))
+
+
+# The 130M model's out-projection (Kr = 96, H = 768, M = 8192 tokens): 48 tiles
+# of dW, six pieces.  Gaussian inputs against the oracle on sampled rows of dW.
+def test_dw_split_130m_out_proj(ops):
+    T, M, Kr, H = 8, 8192, 96, 768
+    _announce(f"dW split 130M out-proj T={T} M={M} Kr={Kr} H={H}")
+    X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=5)
+    dZ = synth.make_grad(T, M, H, seed=5)
+    mask = synth.make_mask(H, 0.5, "random", seed=5)
+    _, dWd = ops.pcr_bwd(G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), need_dx=False)
+    torch.cuda.synchronize()
+    got = G.from_dev_bf16(dWd)
+    _, rdW = oracle.pcr_bwd(dZ, X, W, mask)
+    G.check_bf16(got, rdW, (mask != 0)[None, None, :], "dW split 130M out-proj")
