@@ -94,10 +94,10 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  * products accumulate in fp32.  dX or dW may be NULL to skip that product.
  * Needs caat_pcr_bwd_workspace_bytes() bytes of workspace, any contents on
  * entry: T*M*H*2 (rounded up to 256) for G[T,M,H] (bf16), which it holds on
- * return, plus, when dW has fewer 128x128 tiles than the chip has CUs and
- * M spans at least 16 chunks of 64 tokens, s*T*Kr*H*4 bytes after it for
- * dW's fp32 sums over s pieces of the token range (added in piece order, so
- * the result does not depend on scheduling).
+ * return, plus, when dW's tiles cannot fill the chip's 256 CUs and M spans
+ * at least 16 chunks of 64 tokens, s*T*Kr*H*4 bytes after it for dW's fp32
+ * sums over s pieces of the token range (added in piece order, so the
+ * result does not depend on scheduling).
  * Outputs must not overlap the inputs, the workspace or each other.
  */
 int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask,

@@ -76,22 +76,37 @@ int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, 
   return launched();
 }
 
-// Split of dW's token range: with fewer 128 x 128 tiles than CUs (and no
-// 256 x 256 tiling), dW_t = X_t^T G_t is cut into pieces of at least eight
-// 64-token chunks so that about 256 workgroups run; returns the number of
-// pieces (1: no split) and the chunks per piece.
+// Split of dW's token range when its tiles cannot fill the chip: dW_t =
+// X_t^T G_t is cut into pieces of at least eight 64-token chunks.  With 64
+// to 255 tiles of 256 x 256 those are split into 2-4 pieces, the count that
+// best fills whole rounds of 256 workgroups (192 tiles: 4 pieces, 3 full
+// rounds); with fewer, 128 x 128 tiles are split until about 256 run.
+// splits == 1: no split.
 struct DwSplit {
   int splits, kcs;
+  bool big;
 };
 DwSplit dw_split(int T, int M, int Kr, int H) {
   const int nkm = (M + kBK - 1) / kBK;
-  DwSplit d{1, nkm};
+  DwSplit d{1, nkm, false};
   if (M <= 0 || use_big_tiles(Kr, H, T)) return d;
-  const long long tiles = (long long)((H + 127) / 128) * ((Kr + 127) / 128) * T;
-  if (tiles >= 256) return d;
-  int sp = (int)((256 + tiles - 1) / tiles);
-  if (sp > nkm / 8) sp = nkm / 8;
-  if (sp < 2) return d;
+  const long long big = (long long)((H + 255) / 256) * ((Kr + 255) / 256) * T;
+  int sp = 1;
+  if (big >= 64) {
+    double best = 0.0;
+    for (int c = 2; c <= 4 && c <= nkm / 8; ++c) {
+      const long long n = big * c, rounds = (n + 255) / 256;
+      const double fill = (double)n / (256.0 * (double)rounds);
+      if (fill > best + 1e-9) best = fill, sp = c;
+    }
+    d.big = sp > 1;
+  } else {
+    const long long tiles = (long long)((H + 127) / 128) * ((Kr + 127) / 128) * T;
+    if (tiles >= 256) return d;
+    sp = (int)((256 + tiles - 1) / tiles);
+    if (sp > nkm / 8) sp = nkm / 8;
+  }
+  if (sp < 2) return DwSplit{1, nkm, false};
   d.kcs = (nkm + sp - 1) / sp;
   d.splits = (nkm + d.kcs - 1) / d.kcs;  // every piece has at least one chunk
   return d;
@@ -105,9 +120,15 @@ size_t dw_split_bytes(int T, int M, int Kr, int H) {
 // dW through fp32 pieces in `part` (dw_split_bytes of them), then their sum.
 int launch_dw_split(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, float* part,
                     const DwSplit& d, hipStream_t s) {
-  const int tm = (H + 127) / 128, tn = (Kr + 127) / 128;
-  hipLaunchKernelGGL((pcr_bwd_dw_kernel<128, 128, 4, true>), dim3(T * d.splits * tm * tn), dim3(256), 0, s, G, X,
-                     dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs);
+  if (d.big) {
+    const int tm = (H + 255) / 256, tn = (Kr + 255) / 256;
+    hipLaunchKernelGGL((pcr_bwd_dw_kernel<256, 256, kBigTileWaves, true>), dim3(T * d.splits * tm * tn),
+                       dim3(kBigTileWaves * 64), 0, s, G, X, dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs);
+  } else {
+    const int tm = (H + 127) / 128, tn = (Kr + 127) / 128;
+    hipLaunchKernelGGL((pcr_bwd_dw_kernel<128, 128, 4, true>), dim3(T * d.splits * tm * tn), dim3(256), 0, s, G, X,
+                       dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs);
+  }
   if (int st = launched()) return st;
   const long long n4 = (long long)T * Kr * H / 4;
   hipLaunchKernelGGL(dw_split_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, part, dW, d.splits,

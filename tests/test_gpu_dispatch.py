@@ -133,3 +133,21 @@ def test_dw_split_130m_out_proj(ops):
     got = G.from_dev_bf16(dWd)
     _, rdW = oracle.pcr_bwd(dZ, X, W, mask)
     G.check_bf16(got, rdW, (mask != 0)[None, None, :], "dW split 130M out-proj")
+
+
+# The same with 256x256 tiles: T = 4, Kr = 264, H = 2056 have 72 of them;
+# three pieces (216 workgroups) fill a round best.  M = 1600 tokens is 25
+# chunks: pieces of 9, 9 and 7.
+def test_dw_split_big_tiles_bitexact(ops):
+    T, M, Kr, H = 4, 1600, 264, 2056
+    _announce(f"dW split, 256x256 tiles T={T} M={M} Kr={Kr} H={H}")
+    base = -(-(T * M * H * 2) // 256) * 256
+    assert ops.bwd_workspace_bytes(T, M, Kr, H) - base == 3 * T * Kr * H * 4
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=78, lo=-1, hi=1, x_zero_frac=0.8)
+    dZ = _int_grad(T, M, H, 78, nz=0.2)
+    mask = synth.make_mask(H, 0.5, "random", seed=78)
+    _, rdW = oracle.pcr_bwd(dZ, X, W, mask)
+    assert np.abs(rdW).max() <= 256
+    _, dWd = ops.pcr_bwd(G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), need_dx=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(dWd), rdW)
