@@ -116,6 +116,29 @@ def test_workspace_sizes(L):
     assert L.caat_pcr_bwd_workspace_bytes(0, 8, Kr, H) == 0  # invalid dims report 0
 
 
+def test_bwd_workspace_split_pieces(L):
+    """The backward's workspace: G for every rank, then s fp32 pieces of dW
+    when its tiles cannot fill 256 CUs and M spans at least 16 chunks of 64
+    tokens.  Host-only (nothing is launched)."""
+    L.caat_pcr_bwd_workspace_bytes.restype = ctypes.c_size_t
+
+    def pieces(T, M, Kr, H):
+        g = -(-(T * M * H * 2) // 256) * 256
+        extra = L.caat_pcr_bwd_workspace_bytes(T, M, Kr, H) - g
+        assert extra >= 0 and extra % (T * Kr * H * 4) == 0
+        return extra // (T * Kr * H * 4) or 1
+
+    assert pieces(8, 16384, 1376, 4096) == 1  # 7B down-proj: 768 tiles of 256x256
+    assert pieces(8, 16384, 512, 4096) == 1   # 7B out-proj: 256 of them
+    assert pieces(8, 32768, 704, 2048) == 4   # 1.1B: 192 big tiles x 4 = 3 full rounds
+    assert pieces(8, 32768, 256, 2048) == 4   # 64 big tiles x 4 = one round
+    assert pieces(8, 8192, 384, 768) == 2     # 130M: 144 tiles of 128x128
+    assert pieces(8, 8192, 96, 768) == 6      # 48 of them
+    assert pieces(8, 960, 96, 768) == 1       # 15 chunks: too short to split
+    assert pieces(8, 1024, 96, 768) == 2      # 16 chunks: two pieces of eight
+    assert pieces(2, 256, 1536, 768) == 1     # the tiny layer: 4 chunks
+
+
 def bwd(L, dZ=A, X=B, W=C, mask=D, dX=E, dW=E + (1 << 32), T=4, M=64, Kr=64, H=64, ws=E + (2 << 32), wsb=1 << 20):
     return L.caat_pcr_bwd(dZ, X, W, mask, dX, dW, T, M, Kr, H, ws, wsb, None)
 
