@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
+                    help="tokens of the CPU oracle sample (about 10 s on 16 host threads)")
     ap.add_argument("--reduce-m", default="16384,4096,1,8,32",
                     help="token counts of the reduce leg (<= 32: latency points; counter runs take one at a time)")
     ap.add_argument("--decode-m", default="1,8,32", help="token counts of the decode legs (counter runs take one at a time)")
