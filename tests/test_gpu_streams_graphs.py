@@ -99,3 +99,52 @@ def test_graph_replays_match_eager(ops):
     # the decode workspace's arrival counters are back at zero after the replays
     H_blocks = (H + 127) // 128
     assert int(ws_dec[: 4 * H_blocks].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_graph_replays_split_dw_backward(ops):
+    """A backward whose dW is split over the token range (fp32 pieces in the
+    workspace, then their ordered sum) captured in a graph: 128x128 tiles in
+    seven pieces and 256x256 tiles in three.  Every replay matches eager."""
+    _announce("graph capture of split-dW backwards")
+    dev = G.dev()
+    cases = [(2, 4000, 96, 264, 61), (4, 1600, 264, 2056, 62)]
+    bufs = []
+    for T, M, Kr, H, seed in cases:
+        X_, W_ = synth.make_fwd_inputs(T, M, Kr, H, seed=seed)
+        dZ_ = synth.make_grad(T, M, H, seed=seed)
+        mk = G.to_dev_u8(synth.make_mask(H, 0.5, "random", seed=seed))
+        ws = torch.empty(ops.bwd_workspace_bytes(T, M, Kr, H), dtype=torch.uint8, device=dev)
+        assert ws.numel() > -(-(T * M * H * 2) // 256) * 256  # the split's pieces are in the workspace
+        bufs.append((G.to_dev_bf16(dZ_), G.to_dev_bf16(X_), G.to_dev_bf16(W_), mk, ws,
+                     torch.empty((T, M, Kr), dtype=torch.bfloat16, device=dev),
+                     torch.empty((T, Kr, H), dtype=torch.bfloat16, device=dev)))
+
+    def seq():
+        for dZ, X, W, mk, ws, dX, dW in bufs:
+            ops.pcr_bwd(dZ, X, W, mk, dX=dX, dW=dW, workspace=ws)
+
+    seq()
+    torch.cuda.synchronize()
+    want = [(b[5].clone(), b[6].clone()) for b in bufs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        seq()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for b in bufs:
+            b[5].fill_(0)
+            b[6].fill_(0)
+            b[4].fill_(0x7F)  # stale workspace contents must not matter
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (b, (wx, ww)) in enumerate(zip(bufs, want)):
+            assert torch.equal(b[5].view(torch.int16), wx.view(torch.int16)), (rep, i, "dX")
+            assert torch.equal(b[6].view(torch.int16), ww.view(torch.int16)), (rep, i, "dW")
+        seq()  # eager work between replays
+        torch.cuda.synchronize()
