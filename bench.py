@@ -758,7 +758,17 @@ def cpu_baseline(tokens: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    log(f"cpu oracle on {tokens} tokens, {threads} BLAS threads")
+    host_cores = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    log(f"cpu oracle on {tokens} tokens, {threads} BLAS threads of {host_cores} host cores ({model})")
     X, W = synth.make_fwd_inputs(T, tokens, KR, H, seed=0)
     dZ = synth.make_grad(T, tokens, H, seed=0)
     mask = synth.make_mask(H, P, "random", seed=0)
@@ -771,6 +781,9 @@ def cpu_baseline(tokens: int):
         "value": round(flops / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cores": host_cores,
+        "cpu_model": model,
+        "elementwise_threads": 1,
         "kind": "oracle",
         "sample": f"fwd+bwd of {tokens} of {M} tokens (T={T}, Kr={KR}, H={H}, p={P}), fp64 numpy, {dt:.1f} s",
     }

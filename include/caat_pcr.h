@@ -72,12 +72,15 @@ const char* caat_status_string(int status);
  *   out[t][:, c] = sum_u Y_u[:, c]     for c in S   (same value on every rank)
  *   out[t][:, c] = Y_t[:, c]           for c not in S
  * rounded once to bf16 (nearest even).  `out` must not overlap X, W or mask.
- * Decode-shaped calls (M <= 192, taken 32 tokens at a time) run a
- * weight-streaming kernel that needs caat_rowpar_pcr_fwd_workspace_bytes()
- * bytes of workspace; other M need none (pass NULL, 0).  The workspace starts with ceil(H/128) 32-bit arrival
- * counters (padded to 256 bytes) that must be zero when a call starts; every
- * call leaves them zero again, so zero a new workspace once before its first
- * use.  The rest (fp32 partials of the synced channels) may hold anything.
+ * Decode-shaped calls (M <= 192, taken 32 tokens at a time, H <= 65536)
+ * run a weight-streaming kernel that needs
+ * caat_rowpar_pcr_fwd_workspace_bytes() bytes of workspace; other calls need
+ * none (pass NULL, 0).  The workspace starts with a 2 KiB region of 32-bit
+ * arrival counters (the same size and place for every shape) that must be
+ * zero when a call starts; every call leaves them zero again, so zero a new
+ * workspace once before its first use and it stays valid for calls of any
+ * later shape.  The rest (fp32 partials of the synced channels, from byte
+ * 2048 on) may hold anything.
  */
 int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out,
                         int T, int M, int Kr, int H,
@@ -158,6 +161,8 @@ int caat_residual_rmsnorm(const uint16_t* Z, const uint16_t* R, const uint16_t* 
  *   out[t][:, c] = Y[t][:, c]                                      for c not in S
  * (fp32 sum in that order; bf16 rounds the sum once).  out == Y runs in
  * place and never writes the local channels; otherwise out must not overlap Y.
+ * As for every call, one rank's slice M*H must stay below 2^30 elements
+ * (CAAT_ERR_DIM otherwise).
  */
 int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out,
                                 int T, int M, int H, int dtype, void* stream);

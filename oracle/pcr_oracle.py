@@ -52,6 +52,9 @@ __all__ = [
     "fwd_at",
     "bwd_dx_at",
     "bwd_dw_at",
+    "fwd_rows",
+    "bwd_dx_rows",
+    "bwd_dw_rows",
     "synced_elements",
     "ring_allreduce_bytes_per_rank",
 ]
@@ -228,6 +231,59 @@ def bwd_dw_at(dZ, X, mask, ts, ks, cs) -> np.ndarray:
     out = np.empty(len(ts), dtype=np.float64)
     for i, (t, k, c) in enumerate(zip(ts, ks, cs)):
         out[i] = float(bf16_to_f64(np.asarray(X)[t, :, k]) @ _g_col(dZ, mask, t, c))
+    return out
+
+
+def fwd_rows(X, W, mask, ts, ms) -> np.ndarray:
+    """Whole output rows Z[t,m,:] for each sampled (t,m) -> [n, H]: the sum
+    over ranks of X[u][m,:] @ W[u] on the synced channels, rank t's own
+    X[t][m,:] @ W[t] elsewhere."""
+    X = np.asarray(X)
+    W = np.asarray(W)
+    T = X.shape[0]
+    S = np.asarray(mask) != 0
+    ms = np.asarray(ms)
+    um = np.unique(ms)
+    Y = np.stack([bf16_to_f64(X[u][um, :]) @ bf16_to_f64(W[u]) for u in range(T)])  # [T, len(um), H]
+    total = np.zeros(Y.shape[1:], dtype=np.float64)
+    for u in range(T):
+        total += Y[u]
+    pos = np.searchsorted(um, ms)
+    out = np.empty((len(ts), W.shape[2]), dtype=np.float64)
+    for i, (t, j) in enumerate(zip(ts, pos)):
+        out[i] = np.where(S, total[j], Y[int(t), j])
+    return out
+
+
+def bwd_dx_rows(dZ, W, mask, ts, ms) -> np.ndarray:
+    """Whole rows of the input gradient: dX[t,m,:] = G[t][m,:] @ W[t].T for
+    each sampled (t,m) -> [n, Kr].  G[t][m,:] is rank t's reduced gradient
+    row (the synced channels summed over the ranks, its own values
+    elsewhere)."""
+    out = np.empty((len(ts), np.asarray(W).shape[1]), dtype=np.float64)
+    for t in sorted(set(int(v) for v in ts)):
+        Wt = bf16_to_f64(np.asarray(W)[t])
+        for i in np.flatnonzero(np.asarray(ts) == t):
+            out[i] = _g_row(dZ, mask, t, int(ms[i])) @ Wt.T
+    return out
+
+
+def bwd_dw_rows(dZ, X, mask, ts, ks) -> np.ndarray:
+    """Whole rows of the weight gradient: dW[t,k,:] = X[t][:,k] @ G[t] for
+    each sampled (t,k) -> [n, H], with G[t] rank t's reduced gradient."""
+    dZ = np.asarray(dZ)
+    X = np.asarray(X)
+    T, _, H = dZ.shape
+    S = np.asarray(mask) != 0
+    total = np.zeros(dZ.shape[1:], dtype=np.float64)
+    for u in range(T):
+        total += bf16_to_f64(dZ[u])
+    out = np.empty((len(ts), H), dtype=np.float64)
+    for t in sorted(set(int(v) for v in ts)):
+        Gt = np.where(S, total, bf16_to_f64(dZ[t]))
+        rows = np.flatnonzero(np.asarray(ts) == t)
+        Xk = bf16_to_f64(X[t][:, np.asarray(ks)[rows]])  # [M, n_t]
+        out[rows] = Xk.T @ Gt
     return out
 
 

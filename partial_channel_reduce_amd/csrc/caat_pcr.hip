@@ -189,12 +189,16 @@ const char* caat_status_string(int status) {
 // to six chunks that still beats the tiled kernel, which has too few tiles
 // to fill the chip at these sizes), and one chunk's fp32 partials [32][H]
 // addressable with 32-bit byte offsets.
-static bool use_decode(int M, int H) {
-  return M > 0 && M <= kDecChunkedMaxM && (size_t)kDecMaxM * H * 4 < ((size_t)1 << 31);
-}
+// Up to kDecMaxH channels, so that the arrival counters (one int per
+// 128-channel block) fit a region of fixed size at the head of the
+// workspace: a workspace zeroed once stays valid for every later shape.
+constexpr int kDecMaxH = 65536;
+static bool use_decode(int M, int H) { return M > 0 && M <= kDecChunkedMaxM && H <= kDecMaxH; }
 
-// Arrival counters of the decode kernel: one int per channel block.
-static size_t decode_counter_bytes(int H) { return round256((size_t)((H + kDecCols - 1) / kDecCols) * sizeof(int)); }
+// Arrival counters of the decode kernel: a fixed 2 KiB, whatever H.
+constexpr size_t kDecCounterBytes = (size_t)(kDecMaxH / kDecCols) * sizeof(int);
+static_assert(kDecCounterBytes % 256 == 0, "partials stay 256-byte aligned");
+static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || !use_decode(M, H)) return 0;
@@ -205,10 +209,9 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
 
 namespace {
 
-// Shared by the row-parallel forward (mask = S) and the column-parallel
-// forward (mask == nullptr: nothing synced, no workspace used).
-int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr, int H,
-             void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks of the forward (host only), apart from the workspace.
+int fwd_check_args(const uint16_t* X, const uint16_t* W, const uint8_t* mask, const uint16_t* out, int T, int M,
+                   int Kr, int H) {
   if (int st = check_dims(T, M, Kr, H)) return st;
   // tensors with no elements (M == 0) may be passed as NULL
   if (!W || (M > 0 && (!X || !out))) return CAAT_ERR_NULL;
@@ -216,16 +219,16 @@ int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t
   const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nO = (size_t)T * M * H * 2;
   if (M > 0 && (overlap(out, nO, X, nX) || overlap(out, nO, W, nW) || (mask && overlap(out, nO, mask, H))))
     return CAAT_ERR_ALIAS;
-  const size_t need = mask ? caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) : 0;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return CAAT_ERR_WORKSPACE;
-    if (overlap(workspace, need, out, nO) || overlap(workspace, need, X, nX) || overlap(workspace, need, W, nW) ||
-        overlap(workspace, need, mask, H))
-      return CAAT_ERR_ALIAS;
-  }
+  return CAAT_OK;
+}
+
+// Kernel launches of a validated forward.  `workspace` holds the decode
+// kernel's arrival counters (kDecCounterBytes, zero on entry) and then its
+// fp32 partials; it is only touched for decode-shaped calls with a mask.
+int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
+               int H, void* workspace, hipStream_t s) {
   if (M == 0) return CAAT_OK;
   if (!mask) workspace = nullptr;  // never touched without synced channels
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (use_decode(M, H)) {
     // workspace: the per-block arrival counters, then the fp32 partials
     int* arrivals = static_cast<int*>(workspace);
@@ -258,6 +261,22 @@ int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t
   // 64-token tiles lose (M = 2048: 243 -> 321 us).
   if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 512) return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
   return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
+}
+
+// Shared by the row-parallel forward (mask = S) and the column-parallel
+// forward (mask == nullptr: nothing synced, no workspace used).
+int fwd_impl(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr, int H,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = fwd_check_args(X, W, mask, out, T, M, Kr, H)) return st;
+  const size_t need = mask ? caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) : 0;
+  if (need > 0) {
+    const size_t nX = (size_t)T * M * Kr * 2, nW = (size_t)T * Kr * H * 2, nO = (size_t)T * M * H * 2;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return CAAT_ERR_WORKSPACE;
+    if (overlap(workspace, need, out, nO) || overlap(workspace, need, X, nX) || overlap(workspace, need, W, nW) ||
+        overlap(workspace, need, mask, H))
+      return CAAT_ERR_ALIAS;
+  }
+  return fwd_launch(X, W, mask, out, T, M, Kr, H, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -371,6 +390,9 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
   if (T < 1 || T > kMaxT || M < 0 || H < 8 || H % 8 != 0) return CAAT_ERR_DIM;
   if (!mask || (M > 0 && (!Y || !out))) return CAAT_ERR_NULL;
   if ((long long)T * M * (long long)H > (1LL << 40)) return CAAT_ERR_DIM;
+  // one rank's slice below 2^30 elements, as for every call: the kernels
+  // count its 16-byte vectors in 32 bits
+  if ((long long)M * H >= (1LL << 30)) return CAAT_ERR_DIM;
   if (!aligned(Y, 16) || !aligned(out, 16) || !aligned(mask, 8)) return CAAT_ERR_ALIGN;
   const size_t esz = dtype == CAAT_F32 ? 4 : 2;
   const size_t n = (size_t)T * M * H * esz;

@@ -224,6 +224,13 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // Waiting for the stores' acknowledgement before the arrival is counted
   // orders them; the coherent accesses need no cache write-back or
   // invalidation across the chip's L2 slices.
+  // This handoff rests on gfx950's cache-policy bits, not on the HIP memory
+  // model: the partials go through the sc1 (device-coherent) store and load
+  // forms, which bypass the non-coherent per-XCD L2 for those lines, and the
+  // counter is a relaxed device-scope atomic ordered by s_waitcnt.  A release
+  // / acquire pair would write back and invalidate the whole L2 of the XCD
+  // instead (measured as a per-wave fence: 4x slower).  The bitwise decode
+  // tests (chunked calls, a shared workspace, graph replays) guard it.
   constexpr int kSc1 = 1 << 4;
   auto prs = [&](int u) { return make_rsrc(partial + u * MH, (uint32_t)(MH * 4)); };
   if (inb) {

@@ -91,6 +91,18 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
     keepbits[i] = kb;
   }
 
+  // Mask of the 8-channel chunk this lane stores in every row-order drain
+  // (bit b: channel chc + b synced).  A wholly synced chunk is skipped at the
+  // rank boundaries: the end of the tile writes the synced sums over it.
+  const int ccl = lane % RS::CPR;
+  const int chc = chw + ccl * 8;
+  uint32_t m8 = 0;
+  if (mask != nullptr && chc < H) {
+    const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + chc);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) m8 |= (((b < 4 ? mk[0] : mk[1]) >> (8 * (b & 3))) & 0xffu) ? (1u << b) : 0u;
+  }
+
   f32x16 acc[S::WI][S::WJ];
   zero_acc<BM, BN, NW>(acc);
 
@@ -150,7 +162,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
         const int tok0 = tkw + p * JPP * 32;
         RS::drain(st, JPP * 32, lane, [&](int r, int cc, u32x4 v) {
           const int tok = tok0 + r, ch = chw + cc * 8;
-          if (tok < M && ch < H) st16_nt(ot + (long long)tok * H + ch, v);
+          if (tok < M && ch < H && m8 != 0xffu) st16_nt(ot + (long long)tok * H + ch, v);
         });
         lds_wave_sync();
       }
@@ -183,17 +195,9 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   }
   if (T == 1 || mask == nullptr) return;  // nothing synced to hand to other ranks
   const int rows = min(S::WN, M - tkw);
-  // Mask of this lane's drain chunk (8 channels).  When every chunk of the
-  // wave is all-synced or all-local, synced chunks are written whole;
-  // otherwise each lane takes one channel and writes it where synced.
-  const int ccl = lane % RS::CPR;
-  const int chc = chw + ccl * 8;
-  uint32_t m8 = 0;
-  if (chc < H) {
-    const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + chc);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) m8 |= (((b < 4 ? mk[0] : mk[1]) >> (8 * (b & 3))) & 0xffu) ? (1u << b) : 0u;
-  }
+  // When every chunk of the wave is all-synced or all-local, synced chunks
+  // are written whole; otherwise each lane takes one channel and writes it
+  // where synced (every synced channel, those of wholly synced chunks too).
   if (!__any(m8 != 0u && m8 != 0xffu)) {
     RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
       if (m8 == 0xffu && r < rows) {

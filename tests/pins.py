@@ -29,7 +29,9 @@ import numpy as np
 # every sum is exact, so the two must agree bit for bit.
 # ---------------------------------------------------------------------------
 
-def simulate_devices(X, W, mask):
+def simulate_devices(X, W, mask, sent=None):
+    """Run the model; if `sent` is a list, it receives the number of elements
+    each device put on the ring (both phases)."""
     T = len(X)
     M = len(X[0])
     Kr = len(X[0][0])
@@ -42,6 +44,7 @@ def simulate_devices(X, W, mask):
     send = [[partial[t][m][c] for m in range(M) for c in S] for t in range(T)]
     n = len(S) * M
     bounds = [n * i // T for i in range(T + 1)]
+    nsent = [0] * T
 
     def seg(i):
         i %= T
@@ -51,6 +54,7 @@ def simulate_devices(X, W, mask):
     for s in range(T - 1):
         msgs = [(t, [send[t][j] for j in seg(t - s)]) for t in range(T)]
         for t, payload in msgs:
+            nsent[t] += len(payload)
             dst = (t + 1) % T
             for j, v in zip(seg(t - s), payload):
                 send[dst][j] += v
@@ -58,9 +62,12 @@ def simulate_devices(X, W, mask):
     for s in range(T - 1):
         msgs = [(t, [send[t][j] for j in seg(t + 1 - s)]) for t in range(T)]
         for t, payload in msgs:
+            nsent[t] += len(payload)
             dst = (t + 1) % T
             for j, v in zip(seg(t + 1 - s), payload):
                 send[dst][j] = v
+    if sent is not None:
+        sent[:] = nsent
     out = [[[partial[t][m][c] for c in range(H)] for m in range(M)] for t in range(T)]
     for t in range(T):
         j = 0
@@ -349,3 +356,30 @@ def check_rmsnorm_invariants(fn, seed=12):
     # output row is that sum divided by its root mean square
     S = Z + R
     np.testing.assert_allclose(N1 * np.sqrt(np.mean(S * S, axis=-1, keepdims=True)), S, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Payload of the restricted all-reduce (Abstract and Introduction: the
+# payload falls with the fraction of synced channels).  The device model
+# above counts the elements every device puts on the ring; a helper that
+# prices that traffic must match the count: on average over the devices
+# exactly, and per device whenever the packed buffer splits evenly.
+# ---------------------------------------------------------------------------
+
+def check_ring_bytes(ring_bytes, cases=((1, 2, 4), (2, 3, 5), (3, 2, 6), (4, 3, 8), (5, 2, 5), (8, 4, 16)), seed=0):
+    rng = np.random.default_rng(seed)
+    for T, M, H in cases:
+        X = rng.integers(-2, 3, size=(T, M, 2)).astype(np.float64)
+        W = rng.integers(-2, 3, size=(T, 2, H)).astype(np.float64)
+        for trial in range(4):
+            mask = (rng.random(H) < (trial + 1) / 4).astype(np.uint8)
+            n_ch = int(mask.sum())
+            sent = []
+            simulate_devices(X.tolist(), W.tolist(), mask.tolist(), sent=sent)
+            assert len(sent) == T
+            for esz in (2, 4):
+                got = float(ring_bytes(T, M, n_ch, esz))
+                mean = float(np.mean(sent)) * esz
+                assert abs(got - mean) <= 1e-9 * max(1.0, mean), (T, M, H, n_ch, esz, got, mean)
+                if (M * n_ch) % T == 0:
+                    assert all(s * esz == got for s in sent), (T, M, n_ch, sent, got)

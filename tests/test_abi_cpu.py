@@ -104,9 +104,11 @@ def test_fwd_validation(L):
 def test_workspace_sizes(L):
     T, Kr, H = 8, 1376, 4096
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 193, Kr, H) == 0  # tiled path needs none
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65536) == 2048 + 2 * 8 * 65536 * 4
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65544) == 0  # above 65536 channels: tiled
     for M in (1, 8, 32):
         need = L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H)
-        assert need >= 256 + T * M * H * 4 and need % 256 == 0  # arrival counters + fp32 partials
+        assert need == 2048 + T * M * H * 4  # fixed arrival-counter region + fp32 partials
     # 33 .. 192 tokens run 32 at a time and share one chunk's partials
     for M in (33, 100, 192):
         assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == L.caat_rowpar_pcr_fwd_workspace_bytes(T, 32, Kr, H)
@@ -225,6 +227,14 @@ def test_reduce_validation(L):
     assert red(A, C, A + 256, 8, 16, 64, 0, None) == ALIAS  # partial overlap
     assert red(A, C, D, 8, 0, 64, 0, None) == OK  # empty
     assert red(A, C, A, 8, 0, 64, 1, None) == OK  # in place, empty
+    # one rank's slice must stay below 2^30 elements (the kernels count its
+    # vectors in 32 bits); these sizes would wrap that count, so they are
+    # rejected on the host, in place or not, fp32 or bf16
+    big_m = (1 << 22) + 1  # M * 4096 = 2^34 + 4096 elements
+    assert red(A, C, D, 1, big_m, 4096, 0, None) == DIM
+    assert red(A, C, A, 1, big_m, 4096, 0, None) == DIM
+    assert red(A, C, D, 1, 1 << 23, 4096, 1, None) == DIM  # 2^35 bf16 elements
+    assert red(A, C, D, 2, 1 << 18, 4096, 0, None) == DIM  # exactly 2^30 per rank
 
 
 def test_product_path_fails_loudly_without_library(tmp_path):

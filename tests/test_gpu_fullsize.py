@@ -1,8 +1,10 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times: sampled outputs against the oracle evaluated element by
-element, plus properties that hold at any size (synced channels bitwise
-identical across ranks, run-to-run determinism, exact float32 summation order
-of the standalone reduce)."""
+benchmark times: whole output rows at sampled positions (at least 64K
+elements of every output) against the oracle, plus properties that hold at
+any size (synced channels bitwise identical across ranks, run-to-run
+determinism, exact float32 summation order of the standalone reduce).  The
+complete element-by-element comparison of the Llama2-7B forward is in
+test_gpu_fullsize_7b.py."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +15,18 @@ from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-NSAMPLE = 1536
+MIN_ELEMS = 65536  # compared elements per output at least
+
+
+def _sample_rows(rng, n_outer, n_rows, width):
+    """(outer, row) pairs whose whole rows of `width` elements make at least
+    MIN_ELEMS, always including the first and the last row of the last and
+    the first rank (tile edges)."""
+    n = max(4, -(-MIN_ELEMS // width))
+    o = rng.integers(0, n_outer, size=n)
+    r = rng.integers(0, n_rows, size=n)
+    o[:2], r[:2] = (0, n_outer - 1), (n_rows - 1, 0)
+    return o, r
 
 
 @pytest.fixture(scope="module")
@@ -26,14 +39,6 @@ def ops():
 
 def _announce(msg):
     print(f"[case] {msg}", flush=True)
-
-
-def _samples(rng, n, *sizes):
-    return [rng.integers(0, s, size=n) for s in sizes]
-
-
-def _check_sampled_bf16(got, ref, synced, what):
-    G.check_bf16(got, ref, synced, what)
 
 
 def _gather(t, *idx):
@@ -76,10 +81,11 @@ def test_fwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
     for t in range(1, T):
         assert torch.equal(o16[t][:, S], o16[0][:, S]), f"synced channels differ between rank 0 and {t}"
     rng = np.random.default_rng(7)
-    ts, ms, cs = _samples(rng, NSAMPLE, T, M, H)
-    ref = oracle.fwd_at(X, W, mask, ts, ms, cs)
-    got = oracle.bf16_to_f64(_gather(out, ts, ms, cs))
-    _check_sampled_bf16(got, ref, mask[cs] != 0, f"fwd {name}")
+    ts, ms = _sample_rows(rng, T, M, H)
+    ref = oracle.fwd_rows(X, W, mask, ts, ms)
+    got = oracle.bf16_to_f64(_gather(out, ts, ms))
+    assert got.size >= MIN_ELEMS
+    G.check_bf16(got, ref, (mask != 0)[None, :], f"fwd {name}")
 
 
 @pytest.mark.parametrize(
@@ -108,12 +114,16 @@ def test_bwd_full_size_sampled(ops, name, T, M, Kr, H, kind, p):
     assert torch.equal(dX.view(torch.int16), dX2.view(torch.int16))
     assert torch.equal(dW.view(torch.int16), dW2.view(torch.int16))
     rng = np.random.default_rng(8)
-    ts, ms, ks = _samples(rng, NSAMPLE, T, M, Kr)
-    ref = oracle.bwd_dx_at(dZ, W, mask, ts, ms, ks)
-    G.check_bf16(oracle.bf16_to_f64(_gather(dX, ts, ms, ks)), ref, None, f"dX {name}")
-    ts, ks, cs = _samples(rng, 256, T, Kr, H)
-    ref = oracle.bwd_dw_at(dZ, X, mask, ts, ks, cs)
-    G.check_bf16(oracle.bf16_to_f64(_gather(dW, ts, ks, cs)), ref, mask[cs] != 0, f"dW {name}")
+    ts, ms = _sample_rows(rng, T, M, Kr)
+    ref = oracle.bwd_dx_rows(dZ, W, mask, ts, ms)
+    got = oracle.bf16_to_f64(_gather(dX, ts, ms))
+    assert got.size >= MIN_ELEMS
+    G.check_bf16(got, ref, None, f"dX {name}")
+    ts, ks = _sample_rows(rng, T, Kr, H)
+    ref = oracle.bwd_dw_rows(dZ, X, mask, ts, ks)
+    got = oracle.bf16_to_f64(_gather(dW, ts, ks))
+    assert got.size >= MIN_ELEMS
+    G.check_bf16(got, ref, (mask != 0)[None, :], f"dW {name}")
 
 
 @pytest.mark.parametrize("Kr", [1376, 512])

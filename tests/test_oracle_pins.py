@@ -78,6 +78,40 @@ def test_elementwise_forms_match_simulation():
         assert oracle.bwd_dw_at(dZ, X, mask, [t], [k], [c])[0] == fd
 
 
+def test_row_forms_match_finite_differences():
+    """fwd_rows equals the device simulation's rows; bwd_dx_rows / bwd_dw_rows:
+    every entry of the returned rows equals the central difference of the
+    device simulation's loss (exact on integers)."""
+    rng = np.random.default_rng(12)
+    T, M, Kr, H = 3, 5, 4, 6
+    X = rng.integers(-3, 4, size=(T, M, Kr)).astype(np.float64)
+    W = rng.integers(-3, 4, size=(T, Kr, H)).astype(np.float64)
+    dZ = rng.integers(-3, 4, size=(T, M, H)).astype(np.float64)
+    mask = np.array([0, 1, 1, 0, 1, 0], dtype=np.uint8)
+
+    def loss(Xa, Wa):
+        return float(np.sum(pins.simulate_devices(Xa.tolist(), Wa.tolist(), mask.tolist()) * dZ))
+
+    ts, ms = np.array([2, 0, 1, 2]), np.array([4, 0, 3, 1])
+    Z = pins.simulate_devices(X.tolist(), W.tolist(), mask.tolist())
+    assert np.array_equal(oracle.fwd_rows(X, W, mask, ts, ms), Z[ts, ms, :])
+    rows = oracle.bwd_dx_rows(dZ, W, mask, ts, ms)
+    for i, (t, m) in enumerate(zip(ts, ms)):
+        for k in range(Kr):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[t, m, k] += 1
+            Xm[t, m, k] -= 1
+            assert rows[i, k] == (loss(Xp, W) - loss(Xm, W)) / 2
+    ts, ks = np.array([1, 0, 2, 1]), np.array([3, 0, 2, 1])
+    rows = oracle.bwd_dw_rows(dZ, X, mask, ts, ks)
+    for i, (t, k) in enumerate(zip(ts, ks)):
+        for c in range(H):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[t, k, c] += 1
+            Wm[t, k, c] -= 1
+            assert rows[i, c] == (loss(X, Wp) - loss(X, Wm)) / 2
+
+
 def test_bf16_upcast_is_exact():
     # bf16 patterns with known values: 1.0, -2.0, 0.5, smallest normal 2**-126, 3.140625
     bits = np.array([0x3F80, 0xC000, 0x3F00, 0x0080, 0x4049], dtype=np.uint16)
@@ -98,6 +132,34 @@ def test_payload_scales_with_p(kind, H, p):
     full = oracle.ring_allreduce_bytes_per_rank(T, M, H, 2)
     part = oracle.ring_allreduce_bytes_per_rank(T, M, n, 2)
     assert part == pytest.approx(p * full, rel=0, abs=1e-6)
+
+
+def test_ring_bytes_match_device_simulation():
+    """The ring payload helper equals the elements the message-passing
+    device model actually sends (reduce-scatter + all-gather)."""
+    pins.check_ring_bytes(oracle.ring_allreduce_bytes_per_rank)
+
+
+def _ring_no_factor_two(T, M, n, esz):
+    return oracle.ring_allreduce_bytes_per_rank(T, M, n, esz) / 2
+
+
+def _ring_t_not_t_minus_1(T, M, n, esz):
+    return 2.0 * T / T * M * n * esz if T > 1 else 0.0
+
+
+def _ring_over_t_minus_1(T, M, n, esz):
+    return 2.0 * (T - 1) / max(T - 1, 1) * M * n * esz if T > 1 else 0.0
+
+
+def _ring_all_channels(T, M, n, esz):
+    return 2.0 * (T - 1) / T * M * max(n, 1) * esz * 2 if T > 1 else 0.0
+
+
+@pytest.mark.parametrize("mutant", [_ring_no_factor_two, _ring_t_not_t_minus_1, _ring_over_t_minus_1, _ring_all_channels])
+def test_ring_bytes_pin_rejects_mutants(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_ring_bytes(mutant)
 
 
 def test_strided_half_mask_is_even_channels():
