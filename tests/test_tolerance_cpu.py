@@ -60,3 +60,46 @@ def test_class_violation_is_rejected():
     got[i] = 1e-3 + 0.03  # local rms ~1: above 2e-2 * 1, below 2e-2 * whole rms
     with pytest.raises(AssertionError, match="class"):
         G.check_bf16(got, ref, synced, "planted local")
+
+
+def _emulated_bwd(dZ, X, W, mask):
+    """The backward as documented: G's synced channels rounded once to bf16
+    (fp32 ascending-rank sum), exact products, outputs rounded to bf16."""
+    from partial_channel_reduce_amd import synth  # noqa: F401
+
+    Gt = oracle.partial_channel_reduce(dZ, mask) + G.g_rounding_shift(dZ, mask)[None]
+    Xf, Wf = oracle.bf16_to_f64(X), oracle.bf16_to_f64(W)
+    T = Xf.shape[0]
+    rnd = lambda a: oracle.bf16_to_f64(G.f32_to_bf16_bits_rne(a.astype(np.float32)))  # noqa: E731
+    return (rnd(np.stack([Gt[t] @ Wf[t].T for t in range(T)])), rnd(np.stack([Xf[t].T @ Gt[t] for t in range(T)])))
+
+
+def test_g_rounding_allowance():
+    """A backward with a short contraction (8 tokens) carries the effect of
+    G's bf16 rounding; with the allowance the documented arithmetic passes
+    the whole-tensor bar, an error beyond it still fails, and with no synced
+    channel the allowance is zero."""
+    from partial_channel_reduce_amd import synth
+
+    T, M, Kr, H = 8, 8, 1376, 512
+    X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=11)
+    dZ = synth.make_grad(T, M, H, seed=11)
+    mask = synth.make_mask(H, 0.5, "random", seed=11)
+    rdX, rdW = oracle.pcr_bwd(dZ, X, W, mask)
+    eX, eW = _emulated_bwd(dZ, X, W, mask)
+    with pytest.raises(AssertionError, match="whole tensor"):
+        G.check_bf16(eW, rdW, (mask != 0)[None, None, :], "no allowance")
+    ax, aw = G.bwd_g_allowance(dZ, X, W, mask)
+    G.check_bf16(eX, rdX, None, "dX", extra=ax)
+    G.check_bf16(eW, rdW, (mask != 0)[None, None, :], "dW", extra=aw)
+    i = np.unravel_index(np.argmax(np.abs(rdW)), rdW.shape)
+    bad = eW.copy()
+    bad[i] = rdW[i] - np.sign(rdW[i]) * (0.04 * G.rms(rdW) + G.half_ulp_bf16(rdW[i]) + aw[i])
+    with pytest.raises(AssertionError):
+        G.check_bf16(bad, rdW, (mask != 0)[None, None, :], "planted", extra=aw)
+    ax0, aw0 = G.bwd_g_allowance(dZ, X, W, np.zeros(H, dtype=np.uint8))
+    assert not ax0.any() and not aw0.any()
+    # the row forms used at full size agree with the whole-tensor form
+    ts, ms, ks = np.array([1, 0, 7]), np.array([5, 0, 7]), np.array([3, 1375, 700])
+    assert np.allclose(G.dx_rows_g_allowance(dZ, W, mask, ts, ms), ax[ts, ms])
+    assert np.allclose(G.dw_rows_g_allowance(dZ, X, mask, ts, ks, block=3), aw[ts, ks])
