@@ -88,6 +88,29 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
 
 /*
+ * caat_rowpar_pcr_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with no workspace argument.
+ * Decode-shaped calls use a scratch area owned by the library instead, a
+ * static device array of CAAT_NOALLOC_SCRATCH_BYTES (16 MiB) on each GPU,
+ * held until the process ends; it serves calls whose
+ * caat_rowpar_pcr_fwd_workspace_bytes() is at most that (e.g. T*H <= 131056
+ * channels over all ranks); larger ones return CAAT_ERR_WORKSPACE before
+ * anything is enqueued.  The scratch of the device current at the call is
+ * used (`stream` must belong to it); its arrival counters are cleared by the
+ * call itself (a small fill kernel, no memset).  Every call on one GPU shares
+ * that GPU's scratch, so calls that may overlap on one GPU (different
+ * streams, different threads) race and must be serialised by the caller.
+ * Calls that need no scratch (M > 192, or H > 65536) behave exactly like
+ * caat_rowpar_pcr_fwd.  Neither call allocates; this one calls no hipMalloc,
+ * hipFree or allocating library routine at all.  CAAT_ERR_LAUNCH also covers
+ * a failed lookup of the scratch's device address.
+ */
+#define CAAT_NOALLOC_SCRATCH_BYTES (16u << 20)
+int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out,
+                                int T, int M, int Kr, int H, void* stream);
+
+/*
  * Backward of caat_rowpar_pcr_fwd for per-rank incoming gradients dZ[T,M,H]
  * (bf16).  The partial channel-reduce is linear and self-adjoint, which is
  * the forward/backward agreement the paper's Introduction requires:

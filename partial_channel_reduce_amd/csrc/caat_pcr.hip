@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "decode_kernel.hpp"
 #include "gemm_kernels.hpp"
 #include "norm_kernels.hpp"
@@ -287,6 +289,62 @@ int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mas
                         int Kr, int H, void* workspace, size_t workspace_bytes, void* stream) {
   if (!mask) return CAAT_ERR_NULL;
   return fwd_impl(X, W, mask, out, T, M, Kr, H, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- forward without a caller workspace -----------------------------------
+// Library-owned scratch for the decode kernel's arrival counters and fp32
+// partials, one copy per GPU (each device holds its own instance of this
+// array, at its own address, until the process ends; it starts zeroed).  In
+// host code the array's name is only a host-side stand-in: kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)CAAT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` per device (null: not looked up yet)
+
+// Device address of the current device's scratch, looked up once per device.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CAAT_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return CAAT_ERR_LAUNCH;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return CAAT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T,
+                                int M, int Kr, int H, void* stream) {
+  if (!mask) return CAAT_ERR_NULL;
+  if (int st = fwd_check_args(X, W, mask, out, T, M, Kr, H)) return st;
+  const size_t need = caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H);
+  if (need > kScratchBytes) return CAAT_ERR_WORKSPACE;
+  if (M == 0) return CAAT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (int st = scratch_ptr(&ws)) return st;
+    // The arrival counters must start at zero: clear them with a small fill
+    // kernel (not a memset, so that the call can be captured in a graph).
+    const long long nc = (long long)(kDecCounterBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ws), nc, 0u);
+    if (int st = launched()) return st;
+  }
+  return fwd_launch(X, W, mask, out, T, M, Kr, H, ws, s);
 }
 
 int caat_colpar_fwd(const uint16_t* A, const uint16_t* W, uint16_t* U, int T, int M, int K, int N, void* stream) {

@@ -38,6 +38,7 @@ SIGNATURES = [
     ("caat_status_string", ctypes.c_char_p, [_I]),
     ("caat_rowpar_pcr_fwd", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     ("caat_rowpar_pcr_fwd_workspace_bytes", _S, [_I, _I, _I, _I]),
+    ("caat_rowpar_pcr_fwd_noalloc", _I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     ("caat_pcr_bwd", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     ("caat_pcr_bwd_workspace_bytes", _S, [_I, _I, _I, _I]),
     ("caat_colpar_fwd", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
@@ -143,6 +144,25 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
     st = lib().caat_rowpar_pcr_fwd(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, _ptr(workspace), ws_bytes,
                                    _stream(dev))
     _check(st, "caat_rowpar_pcr_fwd")
+    return out
+
+
+def rowpar_pcr_fwd_noalloc(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """rowpar_pcr_fwd into a caller-provided `out`, with no workspace: the
+    library's per-GPU scratch serves decode-shaped calls (see caat_pcr.h).
+    Calls that may overlap on one GPU must be serialised by the caller."""
+    _require(X, "X", torch.bfloat16, 3)
+    dev = X.device
+    _require(W, "W", torch.bfloat16, 3, dev)
+    _require(mask, "mask", torch.uint8, 1, dev)
+    _require(out, "out", torch.bfloat16, 3, dev)
+    T, M, Kr = X.shape
+    H = W.shape[2]
+    if W.shape[0] != T or W.shape[1] != Kr or mask.shape[0] != H or tuple(out.shape) != (T, M, H):
+        raise ValueError(f"shape mismatch: X{tuple(X.shape)} W{tuple(W.shape)} mask{tuple(mask.shape)} "
+                         f"out{tuple(out.shape)}")
+    st = lib().caat_rowpar_pcr_fwd_noalloc(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, _stream(dev))
+    _check(st, "caat_rowpar_pcr_fwd_noalloc")
     return out
 
 

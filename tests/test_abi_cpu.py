@@ -101,6 +101,22 @@ def test_fwd_validation(L):
     assert fwd(L, M=0) == OK
 
 
+def test_noalloc_fwd_validation(L):
+    """The no-allocation forward checks everything on the host first; shapes
+    whose scratch would exceed the library's fixed area are refused."""
+    na = L.caat_rowpar_pcr_fwd_noalloc
+    assert na(A, B, None, D, 8, 32, 64, 64, None) == NULL
+    assert na(None, B, C, D, 8, 32, 64, 64, None) == NULL
+    assert na(A, B, C, D + 2, 8, 32, 64, 64, None) == ALIGN
+    assert na(A, B, C, A, 8, 32, 64, 64, None) == ALIAS
+    assert na(A, B, C, D, 0, 32, 64, 64, None) == DIM
+    assert na(A, B, C, D, 8, 0, 64, 64, None) == OK  # empty: nothing enqueued
+    # 64 ranks x 65536 channels: 16 MiB of fp32 partials + the counters > the scratch
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(64, 1, 8, 65536) > (16 << 20)
+    assert na(A, B, C, D, 64, 1, 8, 65536, None) == WS
+    assert na(A, B, C, D, 8, 32, 8, 16384, None) == WS  # 2048 + 8*32*16384*4 bytes
+
+
 def test_workspace_sizes(L):
     T, Kr, H = 8, 1376, 4096
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 193, Kr, H) == 0  # tiled path needs none
