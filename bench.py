@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--reduce-m", default="16384,4096,1,8,32",
                     help="token counts of the reduce leg (<= 32: latency points; counter runs take one at a time)")
     ap.add_argument("--decode-m", default="1,8,32", help="token counts of the decode legs (counter runs take one at a time)")
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,shapes,reduce,decode,decode_out,tsweep,colpar,norm,payload,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,shapes,reduce,decode,decode_out,tsweep,colpar,norm,reduce_norm,payload,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -125,7 +125,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar", "norm", "payload", "decode_out", "shapes"}
+                                                         "colpar", "norm", "reduce_norm", "payload", "decode_out", "shapes"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -477,6 +477,33 @@ def main():
         del Zn, Rn, gn, ro, no
         torch.cuda.empty_cache()
 
+    if "reduce_norm" in legs:
+        # The partial channel-reduce of bf16 per-rank activations with the
+        # residual update + RMS norm in its epilogue, against the two-kernel
+        # chain it replaces (bf16 reduce writing Z, then the norm pass reading
+        # it).  Algorithmic bytes: Y and R read, Rout and N written.
+        Yr = randn_bf16((T, M, H))
+        Rr = randn_bf16((T, M, H))
+        gr = (1.0 + 0.1 * torch.randn((H,), generator=gen, device=dev)).to(torch.bfloat16)
+        mkr = mask_dev(H)
+        ro, no, zr = torch.empty_like(Yr), torch.empty_like(Yr), torch.empty_like(Yr)
+        t_f = time_call(lambda: ops.reduce_residual_rmsnorm(Yr, mkr, Rr, gr, 1e-5, r_out=ro, n_out=no), 10)
+
+        def chain():
+            ops.partial_channel_reduce(Yr, mkr, out=zr)
+            ops.residual_rmsnorm(zr, Rr, gr, 1e-5, r_out=ro, n_out=no)
+
+        t_c = time_call(chain, 10)
+        nbytes = 4.0 * T * M * H * 2
+        gbs = nbytes / (t_f * 1e-3) / 1e9
+        res["reduce_residual_rmsnorm"] = {
+            "us": round(t_f * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "chain_us": round(t_c * 1e3, 2), "chain_bytes": 6.0 * T * M * H * 2, "bytes": nbytes,
+        }
+        log(f"reduce+residual+norm fused {t_f*1e3:.1f} us vs chain {t_c*1e3:.1f} us")
+        del Yr, Rr, gr, ro, no, zr
+        torch.cuda.empty_cache()
+
     # ------------------------------------ payload of the in-place reduce vs p
     if "payload" in legs:
         # In place with S = the first p*H channels, the reduce touches only
@@ -551,6 +578,7 @@ def main():
         "t_sweep": res.get("t_sweep"),
         "colpar_up_proj": res.get("colpar_up_proj"),
         "residual_rmsnorm": res.get("residual_rmsnorm"),
+        "reduce_residual_rmsnorm": res.get("reduce_residual_rmsnorm"),
         "decode_down_proj": res.get("decode_down_proj"),
         "decode_out_proj": res.get("decode_out_proj"),
         "payload_inplace_reduce": res.get("payload_inplace_reduce"),

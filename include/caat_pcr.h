@@ -178,6 +178,29 @@ int caat_residual_rmsnorm(const uint16_t* Z, const uint16_t* R, const uint16_t* 
                           uint16_t* N, int T, int M, int H, float eps, void* stream);
 
 /*
+ * The partial channel-reduce with the step after it fused into its epilogue
+ * (paper, Introduction: after the partial reduce each rank's activation is
+ * its own and feeds its own residual stream; the Llama-family blocks of the
+ * reproducibility table then RMS-normalise it).  For per-rank bf16 partial
+ * activations Y[T,M,H] (the row-parallel products before the reduce):
+ *   Z_t     = the partial channel-reduce of Y, as caat_partial_channel_reduce
+ *             with CAAT_BF16 (synced channels: fp32 sum in ascending rank
+ *             order, rounded once; local channels: Y_t)
+ *   Rout[t] = bf16(R[t] + Z_t)
+ *   N[t]    = bf16(Rout row * gamma / sqrt(mean(Rout row^2) + eps))
+ * Z is never written: one pass reads Y and R and writes Rout and N, the same
+ * bits as caat_partial_channel_reduce followed by caat_residual_rmsnorm.
+ * Y, R, Rout, N [T,M,H] bf16; mask [H] uint8; gamma [H] bf16; 0 <= eps
+ * (finite); H <= 8192; one rank's slice M*H below 2^30 elements.
+ * Rout == R updates the residual stream in place; otherwise Rout must not
+ * overlap R.  Neither output may overlap Y, mask or gamma, and N may not
+ * overlap R or Rout.  No workspace.
+ */
+int caat_partial_channel_reduce_residual_rmsnorm(const uint16_t* Y, const uint8_t* mask, const uint16_t* R,
+                                                 const uint16_t* gamma, uint16_t* Rout, uint16_t* N,
+                                                 int T, int M, int H, float eps, void* stream);
+
+/*
  * The partial channel-reduce alone, on given per-rank activations Y[T,M,H]
  * of `dtype` (CAAT_F32 or CAAT_BF16):
  *   out[t][:, c] = Y[0][:, c] + Y[1][:, c] + ... + Y[T-1][:, c]   for c in S

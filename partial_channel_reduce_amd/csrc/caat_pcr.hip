@@ -510,4 +510,56 @@ int caat_residual_rmsnorm(const uint16_t* Z, const uint16_t* R, const uint16_t* 
   return launched();
 }
 
+
+int caat_partial_channel_reduce_residual_rmsnorm(const uint16_t* Y, const uint8_t* mask, const uint16_t* R,
+                                                  const uint16_t* gamma, uint16_t* Rout, uint16_t* N, int T, int M,
+                                                  int H, float eps, void* stream) {
+  if (T < 1 || T > kMaxT || M < 0 || H < 8 || H % 8 != 0 || H > 8 * kNormThreads * kNormMaxVecs) return CAAT_ERR_DIM;
+  if ((long long)M * H >= (1LL << 30)) return CAAT_ERR_DIM;
+  if (!(eps >= 0.0f) || eps > 1e30f) return CAAT_ERR_DIM;  // also rejects NaN
+  if (!mask || !gamma || (M > 0 && (!Y || !R || !Rout || !N))) return CAAT_ERR_NULL;
+  if (!aligned(Y, 16) || !aligned(R, 16) || !aligned(gamma, 16) || !aligned(Rout, 16) || !aligned(N, 16) ||
+      !aligned(mask, 8))
+    return CAAT_ERR_ALIGN;
+  const size_t n = (size_t)T * M * H * 2, ng = (size_t)H * 2;
+  if (M > 0) {
+    const void* ins[3] = {Y, gamma, mask};
+    const size_t nin[3] = {n, ng, (size_t)H};
+    for (int i = 0; i < 3; ++i)
+      if (overlap(Rout, n, ins[i], nin[i]) || overlap(N, n, ins[i], nin[i])) return CAAT_ERR_ALIAS;
+    if (overlap(R, n, Y, n)) return CAAT_ERR_ALIAS;
+    if (Rout != R && overlap(Rout, n, R, n)) return CAAT_ERR_ALIAS;
+    if (overlap(N, n, R, n) || overlap(N, n, Rout, n)) return CAAT_ERR_ALIAS;
+  }
+  if (M == 0) return CAAT_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)M), block(kNormThreads);
+  const long long mh = (long long)M * H;
+  const int hv = H / 8;
+  const int kv = hv <= kNormThreads ? 1 : hv <= 2 * kNormThreads ? 2 : 4;
+#define CAAT_RRN(KV, TC) \
+  hipLaunchKernelGGL((pcr_reduce_residual_rmsnorm_kernel<KV, TC>), grid, block, 0, s, Y, mask, R, gamma, Rout, N, T, H, mh, eps)
+  if (kv == 1) {
+    switch (T) {
+      case 1: CAAT_RRN(1, 1); break;
+      case 2: CAAT_RRN(1, 2); break;
+      case 4: CAAT_RRN(1, 4); break;
+      case 8: CAAT_RRN(1, 8); break;
+      default: CAAT_RRN(1, 0); break;
+    }
+  } else if (kv == 2) {
+    switch (T) {
+      case 1: CAAT_RRN(2, 1); break;
+      case 2: CAAT_RRN(2, 2); break;
+      case 4: CAAT_RRN(2, 4); break;
+      case 8: CAAT_RRN(2, 8); break;
+      default: CAAT_RRN(2, 0); break;
+    }
+  } else {
+    CAAT_RRN(4, 0);
+  }
+#undef CAAT_RRN
+  return launched();
+}
+
 }  // extern "C"

@@ -45,6 +45,7 @@ SIGNATURES = [
     ("caat_colpar_bwd", _I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     ("caat_residual_rmsnorm", _I, [_P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
     ("caat_partial_channel_reduce", _I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    ("caat_partial_channel_reduce_residual_rmsnorm", _I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
 ]
 
 
@@ -288,4 +289,35 @@ def residual_rmsnorm(Z: torch.Tensor, R: torch.Tensor, gamma: torch.Tensor, eps:
     st = lib().caat_residual_rmsnorm(_ptr(Z), _ptr(R), _ptr(gamma), _ptr(r_out), _ptr(n_out), T, M, H, float(eps),
                                      _stream(dev))
     _check(st, "caat_residual_rmsnorm")
+    return r_out, n_out
+
+
+def reduce_residual_rmsnorm(Y: torch.Tensor, mask: torch.Tensor, R: torch.Tensor, gamma: torch.Tensor,
+                            eps: float = 1e-5, r_out: torch.Tensor | None = None, n_out: torch.Tensor | None = None,
+                            inplace: bool = False):
+    """(Rout, N): the partial channel-reduce of bf16 Y[T,M,H] with the residual
+    update and RMS normalisation in its epilogue (see caat_pcr.h); Z is not
+    materialised.  inplace=True writes Rout into R."""
+    _require(Y, "Y", torch.bfloat16, 3)
+    dev = Y.device
+    _require(mask, "mask", torch.uint8, 1, dev)
+    _require(R, "R", torch.bfloat16, 3, dev)
+    _require(gamma, "gamma", torch.bfloat16, 1, dev)
+    T, M, H = Y.shape
+    if tuple(R.shape) != (T, M, H) or gamma.shape[0] != H or mask.shape[0] != H:
+        raise ValueError(f"shape mismatch: Y{tuple(Y.shape)} R{tuple(R.shape)} gamma{tuple(gamma.shape)} "
+                         f"mask{tuple(mask.shape)}")
+    if inplace:
+        r_out = R
+    elif r_out is None:
+        r_out = torch.empty_like(Y)
+    if n_out is None:
+        n_out = torch.empty_like(Y)
+    _require(r_out, "r_out", torch.bfloat16, 3, dev)
+    _require(n_out, "n_out", torch.bfloat16, 3, dev)
+    if tuple(r_out.shape) != (T, M, H) or tuple(n_out.shape) != (T, M, H):
+        raise ValueError("outputs must have Y's shape")
+    st = lib().caat_partial_channel_reduce_residual_rmsnorm(_ptr(Y), _ptr(mask), _ptr(R), _ptr(gamma), _ptr(r_out),
+                                                            _ptr(n_out), T, M, H, float(eps), _stream(dev))
+    _check(st, "caat_partial_channel_reduce_residual_rmsnorm")
     return r_out, n_out

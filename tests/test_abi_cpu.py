@@ -231,6 +231,38 @@ def test_residual_rmsnorm_validation(L):
     assert rms(L, M=0) == OK  # empty: nothing enqueued
 
 
+def test_reduce_residual_rmsnorm_validation(L):
+    """The reduce with the residual update and norm in its epilogue: host-side
+    checks only, every call returns before any launch."""
+    f = L.caat_partial_channel_reduce_residual_rmsnorm
+
+    def call(Y=A, mask=B, R=C, g=D, Ro=E, N=E + (1 << 32), T=4, M=16, H=64, eps=1e-5):
+        return f(Y, mask, R, g, Ro, N, T, M, H, eps, None)
+
+    assert call(Y=None) == NULL
+    assert call(mask=None) == NULL
+    assert call(g=None) == NULL
+    assert call(N=None) == NULL
+    assert call(Y=None, R=None, Ro=None, N=None, M=0) == OK  # empty tensors may be NULL
+    assert call(T=0) == DIM
+    assert call(T=65) == DIM
+    assert call(H=60) == DIM
+    assert call(H=8200) == DIM  # above 8192 channels
+    assert call(M=1 << 18, H=4096) == DIM  # one rank's slice of 2^30 elements
+    assert call(eps=-1.0) == DIM
+    assert call(eps=float("nan")) == DIM
+    assert call(Ro=E + 2) == ALIGN
+    assert call(mask=B + 4) == ALIGN
+    assert call(Ro=A) == ALIAS  # Rout over Y
+    assert call(N=A + 64) == ALIAS  # N over Y
+    assert call(R=A + 128) == ALIAS  # R over Y
+    assert call(Ro=C + 16) == ALIAS  # Rout partly over R (not in place)
+    assert call(N=C) == ALIAS  # N over R
+    assert call(N=E) == ALIAS  # N over Rout
+    assert call(Ro=B) == ALIAS  # Rout over the mask
+    assert call(M=0) == OK  # empty: nothing enqueued
+
+
 def test_reduce_validation(L):
     red = L.caat_partial_channel_reduce
     assert red(None, C, D, 8, 16, 64, 0, None) == NULL
