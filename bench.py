@@ -47,6 +47,7 @@ PAYLOAD_P = (0.25, 0.5, 0.75, 1.0)  # sync fractions of the payload leg (prefix 
 PAYLOAD_CALLS = 3                   # in-place reduce calls per p before its timing
 COPY_KERNEL_KEY = "neg_kernel"  # substring naming torch's elementwise negation kernel
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_7b_down_proj.txt")
+MASK_ORDER = ("random", "prefix", "strided")  # the fwd_masks leg's order
 
 
 def log(*a):
@@ -75,6 +76,8 @@ def parse():
     ap.add_argument("--rocprof-stall", nargs=3, metavar=("SQ_DIR", "TCP_DIR", "TA_DIR"),
                     help="print where the GEMMs' memory path waits (L1 stalls on L2 data, TA/TD busy, L2 hit rate, "
                          "LDS bank conflicts, wave waits) from three rocprofv3 --pmc csv runs of the train leg, and exit")
+    ap.add_argument("--rocprof-masks", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="forward HBM traffic per sync-set kind from two --pmc runs of `--only fwd_masks,copy`, and exit")
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
                          "calibrated against the copy leg's kernel, and exit")
@@ -104,6 +107,9 @@ def main():
     if args.rocprof_stall:
         print(rocprof_stall_summary(*args.rocprof_stall))
         return
+    if args.rocprof_masks:
+        print(rocprof_masks_summary(*args.rocprof_masks))
+        return
     if args.rocprof_traffic:
         print(rocprof_traffic_summary(*args.rocprof_traffic))
         return
@@ -125,7 +131,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar", "norm", "reduce_norm", "payload", "decode_out", "shapes"}
+                                                         "colpar", "norm", "reduce_norm", "fwd_masks", "payload", "decode_out", "shapes"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -477,6 +483,23 @@ def main():
         del Zn, Rn, gn, ro, no
         torch.cuda.empty_cache()
 
+    if "fwd_masks" in legs:
+        # The 7B forward with the three kinds of sync set, in this order (a
+        # counter run splits the forward's dispatches into three equal groups
+        # by dispatch order): a random S, the first half of the channels, the
+        # even channels.  Each kind: 2 warm-up calls, then 5 timed ones.
+        Xm = randn_bf16((T, M, KR))
+        Wm = randn_bf16((T, KR, H), 0.02)
+        om = torch.empty((T, M, H), dtype=torch.bfloat16, device=dev)
+        fm = {}
+        for kind in MASK_ORDER:
+            mkk = mask_dev(H, kind=kind)
+            fm[kind] = round(time_call(lambda: ops.rowpar_pcr_fwd(Xm, Wm, mkk, out=om), 5), 4)
+        res["fwd_masks_ms"] = fm
+        log(f"forward by sync-set kind (ms): {fm}")
+        del Xm, Wm, om
+        torch.cuda.empty_cache()
+
     if "reduce_norm" in legs:
         # The partial channel-reduce of bf16 per-rank activations with the
         # residual update + RMS norm in its epilogue, against the two-kernel
@@ -579,6 +602,7 @@ def main():
         "colpar_up_proj": res.get("colpar_up_proj"),
         "residual_rmsnorm": res.get("residual_rmsnorm"),
         "reduce_residual_rmsnorm": res.get("reduce_residual_rmsnorm"),
+        "fwd_masks_ms": res.get("fwd_masks_ms"),
         "decode_down_proj": res.get("decode_down_proj"),
         "decode_out_proj": res.get("decode_out_proj"),
         "payload_inplace_reduce": res.get("payload_inplace_reduce"),
@@ -770,6 +794,38 @@ def rocprof_traffic_summary(fetch_dir: str, write_dir: str) -> str:
             lines.append(f"`traffic {base} src={cur} bytes={int(rb + wb)} read={int(rb)} write={int(wb)}`")
     return "\n".join(out + ["", "Machine-readable (kernel, kernel-source hash, calibrated bytes per dispatch):", ""]
                      + [ln + "  " for ln in lines])
+
+
+def rocprof_masks_summary(fetch_dir: str, write_dir: str) -> str:
+    """The 256x256 forward's FETCH_SIZE / WRITE_SIZE per sync-set kind: its
+    dispatches in dispatch order split into len(MASK_ORDER) equal groups
+    (the fwd_masks leg runs one kind after the other), scaled by what the
+    counters read for the calibration kernel."""
+    def series(d, counter):
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv")) if r["Counter_Name"] == counter]
+        fw = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                    if "rowpar_pcr_fwd_kernel<256, 256, 8>" in r["Kernel_Name"])
+        cp = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL_KEY in r["Kernel_Name"]]
+        return [v for _, v in fw], sum(cp) / len(cp)
+
+    fetch, cf = series(fetch_dir, "FETCH_SIZE")
+    write, cw = series(write_dir, "WRITE_SIZE")
+    known_kib = COPY_ELEMS * 4 / 1024.0
+    sf, sw = known_kib / cf, known_kib / cw
+    n = len(fetch) // len(MASK_ORDER)
+    out_b = T * M * H * 2
+    algo = 2.0 * M * T * KR + 2.0 * T * KR * H + out_b
+    lines = [f"calibration: FETCH_SIZE scale {sf:.4f}, WRITE_SIZE scale {sw:.4f}; {n} dispatches per kind",
+             "",
+             "| sync set | HBM read MB | HBM write MB | write / output bytes | read + write / algorithmic bytes |",
+             "|---|---|---|---|---|"]
+    for i, kind in enumerate(MASK_ORDER):
+        f = fetch[i * n:(i + 1) * n]
+        w = write[i * n:(i + 1) * n]
+        rb = sum(f) / len(f) * sf * 1024
+        wb = sum(w) / len(w) * sw * 1024
+        lines.append(f"| {kind} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {wb / out_b:.3f} | {(rb + wb) / algo:.3f} |")
+    return "\n".join(lines)
 
 
 def cpu_baseline(tokens: int):
