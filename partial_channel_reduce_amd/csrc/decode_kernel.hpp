@@ -167,15 +167,17 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   __syncthreads();
 
   // Add the waves' partial products in wave order.  Accumulator layout
-  // (16x16): channel 16j + lane%16, token rows 16b + 4*(lane/16) + e.
+  // (16x16): channel 16j + lane%16, token rows 16b + 4*(lane/16) + e.  Only
+  // the M real token rows go through LDS (one of sixteen at M = 1).
   float* red = reinterpret_cast<float*>(lds);  // [waves][16*NB tokens][kDecCols channels]
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int e = 0; e < 4; ++e)
+      if (16 * b + 4 * g + e < M)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[(wave * RR + 16 * b + 4 * g + e) * kDecCols + 16 * j + (lane & 15)] = acc[b][j][e];
+        for (int j = 0; j < NJ; ++j)
+          red[(wave * RR + 16 * b + 4 * g + e) * kDecCols + 16 * j + (lane & 15)] = acc[b][j][e];
   __syncthreads();
   // Each thread takes 4 adjacent channels (16 bytes of fp32) of token rows
   // tid/QPR + RPP*p, p = 0 .. NP-1.
