@@ -84,13 +84,29 @@ def parse():
     return ap.parse_args()
 
 
-def src_hash() -> str:
+# The sources each counted kernel is compiled from (its device code; the host
+# dispatch that picks it is the bench's fixed configuration).
+_GEMM_SOURCES = ("common.hpp", "gemm_core.hpp", "gemm_kernels.hpp", "reduce_kernels.hpp")
+KERNEL_SOURCES = {
+    "rowpar_pcr_fwd_kernel": _GEMM_SOURCES,
+    "pcr_bwd_dx_kernel": _GEMM_SOURCES,
+    "pcr_bwd_dw_kernel": _GEMM_SOURCES,
+    "pcr_reduce_bf16_kernel": ("common.hpp", "reduce_kernels.hpp"),
+}
+
+
+def src_hash(files=None) -> str:
+    """Hash of the kernel sources (all of them, or the given files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "partial_channel_reduce_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_src_hash(kernel: str) -> str:
+    return src_hash(KERNEL_SOURCES.get(kernel))
 
 
 def main():
@@ -621,7 +637,7 @@ def recorded_traffic(kernel: str):
             lines = fh.read().splitlines()
     except OSError:
         return None
-    cur = src_hash()
+    cur = kernel_src_hash(kernel)
     for ln in lines:
         f = ln.strip().strip("`").split()
         if len(f) >= 4 and f[0] == "traffic" and f[1] == kernel and f[2] == f"src={cur}":
@@ -782,7 +798,6 @@ def rocprof_traffic_summary(fetch_dir: str, write_dir: str) -> str:
         "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
         "|---|---|---|---|---|---|",
     ]
-    cur = src_hash()
     lines = []
     for k in sorted(fetch, key=lambda k: -fetch[k]):
         if k not in write:
@@ -790,9 +805,9 @@ def rocprof_traffic_summary(fetch_dir: str, write_dir: str) -> str:
         rb, wb = fetch[k] * sf * 1024, write[k] * sw * 1024
         out.append(f"| {_short(k)} | {nf[k]} | {fetch[k]:.0f} | {write[k]:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
         base = _short(k).split("<")[0]
-        if base.startswith(("rowpar_pcr", "pcr_bwd", "pcr_reduce")):
-            lines.append(f"`traffic {base} src={cur} bytes={int(rb + wb)} read={int(rb)} write={int(wb)}`")
-    return "\n".join(out + ["", "Machine-readable (kernel, kernel-source hash, calibrated bytes per dispatch):", ""]
+        if base in KERNEL_SOURCES:
+            lines.append(f"`traffic {base} src={kernel_src_hash(base)} bytes={int(rb + wb)} read={int(rb)} write={int(wb)}`")
+    return "\n".join(out + ["", "Machine-readable (kernel, hash of that kernel's sources, calibrated bytes per dispatch):", ""]
                      + [ln + "  " for ln in lines])
 
 
