@@ -119,11 +119,16 @@ int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint
  * G's synced channels are rounded to bf16 once (they feed bf16 MFMA); both
  * products accumulate in fp32.  dX or dW may be NULL to skip that product.
  * Needs caat_pcr_bwd_workspace_bytes() bytes of workspace, any contents on
- * entry: T*M*H*2 (rounded up to 256) for G[T,M,H] (bf16), which it holds on
- * return, plus, when dW's tiles cannot fill the chip's 256 CUs and M spans
- * at least 16 chunks of 64 tokens, s*T*Kr*H*4 bytes after it for dW's fp32
- * sums over s pieces of the token range (added in piece order, so the
- * result does not depend on scheduling).
+ * entry and unspecified contents on return: T*M*H*2 (rounded up to 256) for
+ * G[T,M,H] (bf16), then 256 bytes, plus, when dW's tiles cannot fill the
+ * chip's 256 CUs and M spans at least 16 chunks of 64 tokens, s*T*Kr*H*4
+ * bytes after those for dW's fp32 sums over s pieces of the token range
+ * (added in piece order, so the result does not depend on scheduling).
+ * With H <= 16384, G is only written where it differs from dZ per rank:
+ * 256-channel tiles with no synced channel are read from dZ directly, and
+ * tiles whose channels are all synced hold the one sum once (a contiguous S
+ * then forms a fraction p of G instead of all of it); the results are the
+ * same.
  * Outputs must not overlap the inputs, the workspace or each other.
  */
 int caat_pcr_bwd(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uint8_t* mask,

@@ -62,19 +62,24 @@ int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   return launched();
 }
 
+// G: the backward's reduced gradient; with tile classes (tbits != nullptr)
+// only its mixed tiles are per rank, wholly synced ones sit in rank 0's slot
+// and wholly local ones are read from dZ.
 template <int BM, int BN, int NW>
-int launch_dx(const uint16_t* G, const uint16_t* W, uint16_t* dX, int T, int M, int Kr, int H, hipStream_t s) {
+int launch_dx(const uint16_t* G, const uint16_t* W, uint16_t* dX, int T, int M, int Kr, int H, const uint16_t* dZ,
+              const unsigned long long* tbits, hipStream_t s) {
   const int tm = (Kr + BM - 1) / BM, tn = (M + BN - 1) / BN;  // dX column tiles x token tiles
   hipLaunchKernelGGL((pcr_bwd_dx_kernel<BM, BN, NW>), dim3(T * tm * tn), dim3(NW * 64), 0, s, G, W, dX, T, M, Kr,
-                     H, tm, tn);
+                     H, tm, tn, dZ, tbits);
   return launched();
 }
 
 template <int BM, int BN, int NW>
-int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, hipStream_t s) {
+int launch_dw(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, const uint16_t* dZ,
+              const unsigned long long* tbits, hipStream_t s) {
   const int tm = (H + BM - 1) / BM, tn = (Kr + BN - 1) / BN;  // channel tiles x dW row tiles
   hipLaunchKernelGGL((pcr_bwd_dw_kernel<BM, BN, NW>), dim3(T * tm * tn), dim3(NW * 64), 0, s, G, X, dW, T, M, Kr,
-                     H, tm, tn, nullptr, 1, (M + kBK - 1) / kBK);
+                     H, tm, tn, nullptr, 1, (M + kBK - 1) / kBK, dZ, tbits);
   return launched();
 }
 
@@ -121,15 +126,16 @@ size_t dw_split_bytes(int T, int M, int Kr, int H) {
 
 // dW through fp32 pieces in `part` (dw_split_bytes of them), then their sum.
 int launch_dw_split(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, int M, int Kr, int H, float* part,
-                    const DwSplit& d, hipStream_t s) {
+                    const DwSplit& d, const uint16_t* dZ, const unsigned long long* tbits, hipStream_t s) {
   if (d.big) {
     const int tm = (H + 255) / 256, tn = (Kr + 255) / 256;
     hipLaunchKernelGGL((pcr_bwd_dw_kernel<256, 256, kBigTileWaves, true>), dim3(T * d.splits * tm * tn),
-                       dim3(kBigTileWaves * 64), 0, s, G, X, dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs);
+                       dim3(kBigTileWaves * 64), 0, s, G, X, dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs, dZ,
+                       tbits);
   } else {
     const int tm = (H + 127) / 128, tn = (Kr + 127) / 128;
     hipLaunchKernelGGL((pcr_bwd_dw_kernel<128, 128, 4, true>), dim3(T * d.splits * tm * tn), dim3(256), 0, s, G, X,
-                       dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs);
+                       dW, T, M, Kr, H, tm, tn, part, d.splits, d.kcs, dZ, tbits);
   }
   if (int st = launched()) return st;
   const long long n4 = (long long)T * Kr * H / 4;
@@ -148,8 +154,11 @@ static uint32_t reduce_groups(const dim3& grid, long long slice_bytes) {
   return grid.x % g == 0 ? g : 1u;
 }
 
-// bf16 partial channel-reduce of y[T,M,H] into o (o == y: in place).
-int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, hipStream_t s) {
+// bf16 partial channel-reduce of y[T,M,H] into o (o == y: in place).  With
+// tbits (the backward's G, out of place), wholly local tiles of channels are
+// skipped and wholly synced ones written to rank 0's slot only.
+int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, hipStream_t s,
+                       const unsigned long long* tbits = nullptr) {
   const long long mh = (long long)M * H;
   const uint32_t nvec = (uint32_t)(mh / 8);
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
@@ -157,10 +166,10 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
   const uint32_t hv = (uint32_t)(H / 8);
   const uint32_t hf = reduce_groups(grid, mh * 2);
   switch (T) {
-    case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
-    case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
-    case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
-    default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+    case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
+    case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
+    case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
+    default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
   }
   return launched();
 }
@@ -351,10 +360,14 @@ int caat_colpar_fwd(const uint16_t* A, const uint16_t* W, uint16_t* U, int T, in
   return fwd_impl(A, W, nullptr, U, T, M, K, N, nullptr, 0, stream);
 }
 
+// The backward's tile classes of channels (two 64-bit masks), after G.
+constexpr size_t kClassBytes = 256;
+
 size_t caat_pcr_bwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK || M == 0) return 0;
-  // G_t for every rank (bf16), then dW's fp32 token-range pieces when dW is split
-  return round256((size_t)T * M * H * 2) + dw_split_bytes(T, M, Kr, H);
+  // G_t for every rank (bf16), the 256-byte tile-class area, then dW's fp32
+  // token-range pieces when dW is split
+  return round256((size_t)T * M * H * 2) + kClassBytes + dw_split_bytes(T, M, Kr, H);
 }
 
 }  // extern "C"
@@ -399,29 +412,40 @@ int bwd_impl(const uint16_t* dZ, const uint16_t* X, const uint16_t* W, const uin
     }
     return CAAT_OK;
   }
-  // G_t = the partial channel-reduce of dZ, for every rank, into the
-  // workspace; with nothing synced G is dZ.
+  // G_t = the partial channel-reduce of dZ, into the workspace; with nothing
+  // synced G is dZ.  Up to 64 tiles of 256 channels (H <= 16384) are first
+  // classified: G is then written only for mixed tiles (every rank) and
+  // wholly synced ones (rank 0's slot, the one sum); the products read a
+  // wholly local tile straight from dZ.  Same values either way.
   const uint16_t* G = dZ;
+  const unsigned long long* tbits = nullptr;
+  const size_t g_bytes = round256((size_t)T * M * H * 2);
   if (mask) {
     uint16_t* Gw = reinterpret_cast<uint16_t*>(workspace);
-    if (int st = launch_reduce_bf16(dZ, mask, Gw, T, M, H, s)) return st;
+    if (H <= kClassCols * kMaxClassTiles) {
+      unsigned long long* tb = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + g_bytes);
+      hipLaunchKernelGGL(pcr_tile_class_kernel, dim3(1), dim3(64), 0, s, mask, H, tb);
+      if (int st = launched()) return st;
+      tbits = tb;
+    }
+    if (int st = launch_reduce_bf16(dZ, mask, Gw, T, M, H, s, tbits)) return st;
     G = Gw;
   }
   if (dX) {
-    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256, kBigTileWaves>(G, W, dX, T, M, Kr, H, s)
-                                           : launch_dx<128, 128, 4>(G, W, dX, T, M, Kr, H, s);
+    const int st = use_big_tiles(M, Kr, T) ? launch_dx<256, 256, kBigTileWaves>(G, W, dX, T, M, Kr, H, dZ, tbits, s)
+                                           : launch_dx<128, 128, 4>(G, W, dX, T, M, Kr, H, dZ, tbits, s);
     if (st) return st;
   }
   if (dW) {
     const DwSplit d = dw_split(T, M, Kr, H);
     int st;
-    if (mask && d.splits > 1)  // the pieces live in the workspace, after G
+    if (mask && d.splits > 1)  // the pieces live in the workspace, after G and the tile classes
       st = launch_dw_split(G, X, dW, T, M, Kr, H,
-                           reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)T * M * H * 2)),
-                           d, s);
+                           reinterpret_cast<float*>(static_cast<char*>(workspace) + g_bytes + kClassBytes), d, dZ,
+                           tbits, s);
     else
-      st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256, kBigTileWaves>(G, X, dW, T, M, Kr, H, s)
-                                   : launch_dw<128, 128, 4>(G, X, dW, T, M, Kr, H, s);
+      st = use_big_tiles(Kr, H, T) ? launch_dw<256, 256, kBigTileWaves>(G, X, dW, T, M, Kr, H, dZ, tbits, s)
+                                   : launch_dw<128, 128, 4>(G, X, dW, T, M, Kr, H, dZ, tbits, s);
     if (st) return st;
   }
   return CAAT_OK;

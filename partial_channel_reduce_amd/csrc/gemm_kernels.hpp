@@ -26,6 +26,13 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// A 64-bit value every lane holds the same copy of, made wave-uniform (scalar).
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Orders this wave's LDS writes before its following LDS reads (and keeps the
 // compiler from moving memory accesses across it).
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -236,7 +243,8 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 template <int BM, int BN, int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
 pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W, uint16_t* __restrict__ dX,
-                  int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
+                  int T, int M, int Kr, int H, int tiles_m, int tiles_n, const uint16_t* __restrict__ dZ,
+                  const unsigned long long* __restrict__ tbits) {
   using S = TileShape<BM, BN, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -256,9 +264,22 @@ pcr_bwd_dx_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ W
   zero_acc<BM, BN, NW>(acc);
 
   const KcDma da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
-  const KcDma db(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
+  KcDma db(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
+  // With tile classes, chunk c's columns of G_t come from dZ_t (a wholly
+  // local tile of channels), from rank 0's slot (wholly synced: the one sum)
+  // or from G_t itself (mixed); the three buffers share one layout.
+  unsigned long long sbits = 0, lbits = 0;
+  if (tbits != nullptr) {
+    sbits = uniform64(tbits[0]);
+    lbits = uniform64(tbits[1]);
+  }
   auto issue = [&](int c) {
     uint16_t* buf = smem + (c & 1) * S::BUF;
+    if (tbits != nullptr) {
+      const int tile = (c * kBK) / kClassCols;
+      const uint16_t* src = ((lbits >> tile) & 1ull) ? dZ + t * MH : ((sbits >> tile) & 1ull) ? G : G + t * MH;
+      db.rsrc = make_rsrc((const void*)uniform64((unsigned long long)(uintptr_t)src), (uint32_t)(MH * 2));
+    }
     da.load<BM, NW>(H, k0r, c * kBK, buf, wave);
     db.load<BN, NW>(H, m0, c * kBK, buf + BM * kBK, wave);
   };
@@ -331,7 +352,7 @@ template <int BM, int BN, int NW, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64, 1)
 pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X, uint16_t* __restrict__ dW,
                   int T, int M, int Kr, int H, int tiles_m, int tiles_n, float* __restrict__ part, int splits,
-                  int kcs) {
+                  int kcs, const uint16_t* __restrict__ dZ, const unsigned long long* __restrict__ tbits) {
   using S = TileShape<BM, BN, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -356,7 +377,19 @@ pcr_bwd_dw_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ X
   f32x16 acc[S::WI][S::WJ];
   zero_acc<BM, BN, NW>(acc);
 
-  const MnDma<BM> da(G + t * MH, (uint32_t)(MH * 2), H, lane, wave);
+  // With tile classes, this tile's channels of G_t come from dZ_t (wholly
+  // local), from rank 0's slot (wholly synced) or from G_t (mixed).  BM <= 256
+  // and c0 is a multiple of BM, so the tile lies in one class tile.
+  const uint16_t* gsrc = G + t * MH;
+  if (tbits != nullptr) {
+    const int tile = c0 / kClassCols;
+    if ((uniform64(tbits[1]) >> tile) & 1ull)
+      gsrc = dZ + t * MH;
+    else if ((uniform64(tbits[0]) >> tile) & 1ull)
+      gsrc = G;
+    gsrc = (const uint16_t*)uniform64((unsigned long long)(uintptr_t)gsrc);
+  }
+  const MnDma<BM> da(gsrc, (uint32_t)(MH * 2), H, lane, wave);
   const MnDma<BN> db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
   auto issue = [&](int c) {
     uint16_t* buf = smem + (c & 1) * S::BUF;

@@ -97,6 +97,35 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
   }
 }
 
+// ---- classes of 256-channel tiles, for the backward's reduced gradient -------
+// With a contiguous sync set most tiles of channels are wholly synced or
+// wholly local.  Then the backward's G needs no per-rank copy there: a wholly
+// local tile of G_t is dZ_t itself, and a wholly synced one is the same sum
+// for every rank, stored once (in rank 0's slot).  tbits[0] has bit i set when
+// every channel of tile i (channels 256 i .. 256 i + 255, or up to H) is
+// synced, tbits[1] when none is; tiles up to kMaxClassTiles (H <= 16384).
+constexpr int kClassCols = 256;
+constexpr int kMaxClassTiles = 64;
+
+__device__ __forceinline__ bool no_zero_byte(uint32_t w) { return ((w - 0x01010101u) & ~w & 0x80808080u) == 0u; }
+
+__global__ void __launch_bounds__(64) pcr_tile_class_kernel(const uint8_t* __restrict__ mask, int H,
+                                                            unsigned long long* tbits) {
+  const int c0 = threadIdx.x * kClassCols;  // one tile per lane
+  bool all = c0 < H, none = c0 < H;
+  const int c1 = min(H, c0 + kClassCols);
+  for (int c = c0; c < c1; c += 8) {  // H % 8 == 0
+    const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
+    all = all && no_zero_byte(mk[0]) && no_zero_byte(mk[1]);
+    none = none && (mk[0] | mk[1]) == 0u;
+  }
+  const unsigned long long sb = __ballot(all), lb = __ballot(none);
+  if (threadIdx.x == 0) {
+    tbits[0] = sb;
+    tbits[1] = lb;
+  }
+}
+
 // ---- bf16: one thread per 8-channel, 16-byte vector ---------------------------
 
 __device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float f[8]) {
@@ -121,13 +150,22 @@ template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint16_t* out,
                        int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace,
-                       uint32_t groups) {
+                       uint32_t groups, const unsigned long long* __restrict__ tbits) {
   const int T = TC > 0 ? TC : T_rt;
   constexpr int NR = TC > 0 ? TC : 1;  // ranks kept in registers
   const uint32_t v = reduce_block(groups) * kReduceThreads + threadIdx.x;
   if (v >= nvec) return;
   const int c = (int)(v % hvec) * 8;
   const long long base = (long long)v * 8;
+  // The backward's G with tile classes (tbits != nullptr, never in place):
+  // nothing to write for a wholly local tile, one copy (rank 0's slot) of
+  // the sum for a wholly synced one.
+  int ranks_out = T;
+  if (tbits != nullptr) {
+    const int tile = c / kClassCols;
+    if ((tbits[1] >> tile) & 1ull) return;
+    if ((tbits[0] >> tile) & 1ull) ranks_out = 1;
+  }
   const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
   if (inplace && (mk[0] | mk[1]) == 0u) return;
   const u32x4 sel = expand_mask8(mk[0], mk[1]);
@@ -158,7 +196,7 @@ pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint
 #pragma unroll
   for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
 #pragma unroll 8
-  for (int t = 0; t < T; ++t) {
+  for (int t = 0; t < ranks_out; ++t) {
     uint16_t* o = out + t * mh + base;
     if (!inplace || all) {
       const u32x4 yt = TC > 0 ? y[t < NR ? t : 0] : ld16(Y + t * mh + base);

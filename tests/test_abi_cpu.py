@@ -141,7 +141,7 @@ def test_bwd_workspace_split_pieces(L):
     L.caat_pcr_bwd_workspace_bytes.restype = ctypes.c_size_t
 
     def pieces(T, M, Kr, H):
-        g = -(-(T * M * H * 2) // 256) * 256
+        g = -(-(T * M * H * 2) // 256) * 256 + 256  # G, then the tile-class area
         extra = L.caat_pcr_bwd_workspace_bytes(T, M, Kr, H) - g
         assert extra >= 0 and extra % (T * Kr * H * 4) == 0
         return extra // (T * Kr * H * 4) or 1
