@@ -62,6 +62,19 @@ int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   return launched();
 }
 
+// The forward with the earlier ranks' tiles held in registers (2 <= T <= 8).
+template <int BM, int BN, int NW>
+int launch_fwd_rb(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
+                  int H, hipStream_t s) {
+  const int tm = (H + BM - 1) / BM, tn = (M + BN - 1) / BN;
+  const dim3 grid(tm * tn), block(NW * 64);
+  if (T <= 4)
+    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 4>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm, tn);
+  else
+    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 8>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm, tn);
+  return launched();
+}
+
 // G: the backward's reduced gradient; with tile classes (tbits != nullptr)
 // only its mixed tiles are per rank, wholly synced ones sit in rank 0's slot
 // and wholly local ones are read from dZ.
@@ -270,7 +283,16 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   // same bits: 130M down-proj (384 tiles) 100 -> 91 us, out-proj 74 -> 68 us,
   // 7B down-proj at M = 1024 (256 tiles) 179 -> 154 us; at 512-1023 tiles the
   // 64-token tiles lose (M = 2048: 243 -> 321 us).
-  if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 512) return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
+  if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 512) {
+    // The earlier ranks' tiles held in registers: with T <= 4 (three
+    // workgroups per CU still fit) and, at one per CU, for contractions of
+    // at most two chunks per rank.  Measured, same bits, M = 8192, H = 768,
+    // random S: Kr = 384, T = 2 22.5 -> 18.8 us, T = 4 45.3 -> 34.0 us;
+    // Kr = 96, T = 8 67.3 -> 61.0 us (at Kr = 384, T = 8 it loses, 93 -> 119).
+    if (mask != nullptr && T >= 2 && (T <= 4 || (T <= 8 && Kr <= 2 * kBK)))
+      return launch_fwd_rb<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
+    return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
+  }
   return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
 }
 

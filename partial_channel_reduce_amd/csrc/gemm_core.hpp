@@ -278,6 +278,16 @@ struct RowStage {
       *reinterpret_cast<u32x2*>(st + off(r, c) + (lane >> 5) * 4) = v;
     }
   }
+  // The same from bf16 already packed in pairs: word w holds the values of
+  // accumulator registers 2w and 2w+1.
+  static __device__ __forceinline__ void put_packed(uint16_t* st, const uint32_t (&p)[8], int i, int row0, int lane) {
+    const int r = row0 + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x2 v = {p[2 * q], p[2 * q + 1]};
+      *reinterpret_cast<u32x2*>(st + off(r, i * 4 + q) + (lane >> 5) * 4) = v;
+    }
+  }
   // Rows 0 .. nrows-1 in row order: store(r, c, v) gets chunk c of row r.
   template <class F>
   static __device__ __forceinline__ void drain(const uint16_t* st, int nrows, int lane, F&& store) {

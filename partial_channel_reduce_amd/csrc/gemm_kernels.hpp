@@ -231,6 +231,159 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 }
 
 // ============================================================================
+// Forward with the earlier ranks' tiles held in registers (2 <= T <= TB, the
+// small tiles only).  The contraction is walked as in the kernel above (the
+// same MFMAs in the same order), but at the end of rank t < T-1 each wave
+// packs its accumulators to bf16 into a register queue and restarts the
+// local channels: no LDS, barrier or store at a rank boundary.  At the end of
+// the tile every rank's output is assembled in registers -- synced channels
+// the sum, local channels that rank's own value -- and written once, whole
+// lines through LDS.  Same bits as the kernel above; each output line is
+// written once whatever S is (no second, partial-line write of the synced
+// channels), and small contractions lose the per-rank drains.  The queue
+// shifts by one slot per rank (static register indices), so the rank loop
+// needs no unrolling.  It costs (T-1) x 16 registers per 32x32 block: with
+// a 128x64 tile, T <= 4 keeps three workgroups per CU, T <= 8 only one.
+// ============================================================================
+template <int BM, int BN, int NW, int TB>
+__global__ void __launch_bounds__(NW * 64, 1)
+rowpar_pcr_fwd_rb_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                         const uint8_t* __restrict__ mask, uint16_t* __restrict__ out, int T, int M, int Kr, int H,
+                         int tiles_m, int tiles_n) {
+  using S = TileShape<BM, BN, NW>;
+  using RS = RowStage<S::WM>;
+  static_assert(TB >= 2 && TB <= 8, "ranks held in registers");
+  static_assert(NW * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  int tm, tn;
+  tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int c0 = tm * BM, m0 = tn * BN;  // channel tile, token tile
+  const int chw = c0 + wm * S::WM;       // this wave's first channel
+  const int tkw = m0 + wn * S::WN;       // this wave's first token
+  const int nk = (Kr + kBK - 1) / kBK;
+  const int kv_last = Kr - (nk - 1) * kBK;
+  const int nchunks = T * nk;
+  const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
+
+  // keepbits[i] bit e: accumulator register e of block i holds a synced
+  // channel (the same layout as in the kernel above).
+  uint32_t keepbits[S::WI];
+#pragma unroll
+  for (int i = 0; i < S::WI; ++i) {
+    uint32_t kb = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ch = chw + (lane >> 5) * 4 + i * 32 + q * 8;
+      const uint32_t m4 = ch < H ? *reinterpret_cast<const uint32_t*>(mask + ch) : 0u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kb |= ((m4 >> (8 * r)) & 0xffu) ? (1u << (4 * q + r)) : 0u;
+    }
+    keepbits[i] = kb;
+  }
+
+  f32x16 acc[S::WI][S::WJ];
+  zero_acc<BM, BN, NW>(acc);
+  // Queue of the finished ranks' tiles (bf16 pairs): slot 0 is the latest
+  // rank; after the loop slot k holds rank T-2-k.
+  uint32_t pk[TB - 1][S::WI][S::WJ][8] = {};
+
+  auto issue = [&](int c) {
+    const int t = c / nk;
+    const int k0 = (c - t * nk) * kBK;
+    uint16_t* buf = smem + (c & 1) * S::BUF;
+    const MnDma<BM> da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
+    const KcDma db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
+    da.template load<NW>(H, c0, k0, buf, wave);
+    db.load<BN, NW>(Kr, m0, k0, buf + BM * kBK, wave);
+  };
+
+  issue(0);
+  for (int t = 0; t < T; ++t) {
+    for (int kc = 0; kc < nk; ++kc) {
+      const int c = t * nk + kc;
+      uint16_t* As = smem + (c & 1) * S::BUF;
+      uint16_t* Bs = As + BM * kBK;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kc == nk - 1 && kv_last < kBK) {  // W's rows past Kr arrived as zeros
+        zero_kcont_tail<BN, S::THREADS>(Bs, kv_last, tid);
+        __syncthreads();
+      }
+      mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
+                            [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                            [&] {
+                              if (c + 1 < nchunks) issue(c + 1);
+                            });
+    }
+    if (t < T - 1) {  // rank t's tile into the queue; the local channels restart
+#pragma unroll
+      for (int k = TB - 2; k >= 1; --k)
+#pragma unroll
+        for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+          for (int j = 0; j < S::WJ; ++j)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) pk[k][i][j][w] = pk[k - 1][i][j][w];
+#pragma unroll
+      for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+        for (int j = 0; j < S::WJ; ++j) {
+#pragma unroll
+          for (int w = 0; w < 8; ++w) pk[0][i][j][w] = pack_bf16x2(acc[i][j][2 * w], acc[i][j][2 * w + 1]);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t keep = (uint32_t)((int)(keepbits[i] << (31 - e)) >> 31);
+            acc[i][j][e] = __uint_as_float(__float_as_uint(acc[i][j][e]) & keep);
+          }
+        }
+    }
+  }
+
+  // The accumulators hold the synced sums and the last rank's local values.
+  __syncthreads();  // every wave is done with the operand buffers
+  uint16_t* st = smem + wave * (S::WM * S::WN);
+  // Ranks T-1, T-2, ..., 0: the last straight from the accumulators, each
+  // earlier one the sums on synced channels and queue slot 0 elsewhere; the
+  // queue then shifts down.
+  for (int u = T - 1; u >= 0; --u) {
+#pragma unroll
+    for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+      for (int j = 0; j < S::WJ; ++j) {
+        uint32_t v[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const uint32_t sw = pack_bf16x2(acc[i][j][2 * w], acc[i][j][2 * w + 1]);
+          const uint32_t km = (((keepbits[i] >> (2 * w)) & 1u) ? 0xffffu : 0u) |
+                              (((keepbits[i] >> (2 * w + 1)) & 1u) ? 0xffff0000u : 0u);
+          v[w] = u == T - 1 ? sw : (sw & km) | (pk[0][i][j][w] & ~km);
+        }
+        RS::put_packed(st, v, i, j * 32, lane);
+      }
+    if (u < T - 1) {
+#pragma unroll
+      for (int k = 0; k + 1 < TB - 1; ++k)
+#pragma unroll
+        for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+          for (int j = 0; j < S::WJ; ++j)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) pk[k][i][j][w] = pk[k + 1][i][j][w];
+    }
+    lds_wave_sync();
+    uint16_t* ou = out + u * MH;
+    RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
+      const int tok = tkw + r, ch = chw + cc * 8;
+      if (tok < M && ch < H) st16_nt(ou + (long long)tok * H + ch, v);
+    });
+    lds_wave_sync();  // the drain's reads are done before the next rank's puts
+  }
+}
+
+// ============================================================================
 // Backward.  G_t (the reduced incoming gradient: the sum over ranks on synced
 // channels, rank t's own gradient elsewhere -- the same partial channel-reduce
 // applied to dZ) is materialised beforehand for every rank, so both products
