@@ -113,11 +113,16 @@ __global__ void __launch_bounds__(64) pcr_tile_class_kernel(const uint8_t* __res
                                                             unsigned long long* tbits) {
   const int c0 = threadIdx.x * kClassCols;  // one tile per lane
   bool all = c0 < H, none = c0 < H;
-  const int c1 = min(H, c0 + kClassCols);
-  for (int c = c0; c < c1; c += 8) {  // H % 8 == 0
-    const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
-    all = all && no_zero_byte(mk[0]) && no_zero_byte(mk[1]);
-    none = none && (mk[0] | mk[1]) == 0u;
+  // All of the lane's 8-byte mask words are loaded at once (no early exit);
+  // words past H count as neither.
+#pragma unroll
+  for (int i = 0; i < kClassCols / 8; ++i) {  // H % 8 == 0
+    const int c = c0 + 8 * i;
+    if (c < H) {
+      const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
+      all &= no_zero_byte(mk[0]) & no_zero_byte(mk[1]);
+      none &= (mk[0] | mk[1]) == 0u;
+    }
   }
   const unsigned long long sb = __ballot(all), lb = __ballot(none);
   if (threadIdx.x == 0) {
