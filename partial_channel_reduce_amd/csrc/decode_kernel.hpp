@@ -230,8 +230,10 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // model: the partials go through the sc1 (device-coherent) store and load
   // forms, which bypass the non-coherent per-XCD L2 for those lines, and the
   // counter is a relaxed device-scope atomic ordered by s_waitcnt.  A release
-  // / acquire pair would write back and invalidate the whole L2 of the XCD
-  // instead (measured as a per-wave fence: 4x slower).  The bitwise decode
+  // / acquire pair writes back and invalidates the whole L2 of the XCD
+  // instead: as a per-wave fence 4x slower; on the one arrival atomic per
+  // workgroup (acq_rel, agent scope, plain partial accesses; same bits)
+  // M = 1 / 8 / 32 took 21.5 / 23.1 / 28.2 us against 18.8 / 19.3 / 23.0.  The bitwise decode
   // tests (chunked calls, a shared workspace, graph replays) guard it.
   constexpr int kSc1 = 1 << 4;
   auto prs = [&](int u) { return make_rsrc(partial + u * MH, (uint32_t)(MH * 4)); };
