@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--reduce-m", default="16384,4096,1,8,32",
                     help="token counts of the reduce leg (<= 32: latency points; counter runs take one at a time)")
     ap.add_argument("--decode-m", default="1,8,32", help="token counts of the decode legs (counter runs take one at a time)")
-    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,shapes,reduce,decode,decode_out,tsweep,colpar,norm,reduce_norm,payload,copy (profiling runs)")
+    ap.add_argument("--only", default="", help="comma list of legs: train,context,out,shapes,reduce,decode,decode_out,mid,tsweep,colpar,norm,reduce_norm,payload,copy (profiling runs)")
     ap.add_argument("--rocprof-stats", metavar="DIR", help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--rocprof-mfma", metavar="DIR",
                     help="print per-kernel MfmaUtil and performed bf16 MFMA flops from a rocprofv3 "
@@ -147,7 +147,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     legs = set(args.only.split(",")) if args.only else {"train", "context", "out", "reduce", "decode", "tsweep",
-                                                         "colpar", "norm", "reduce_norm", "fwd_masks", "payload", "decode_out", "shapes"}
+                                                         "colpar", "norm", "reduce_norm", "fwd_masks", "payload", "decode_out", "shapes",
+                                                         "mid"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
@@ -413,6 +414,36 @@ def main():
         del Ws
         torch.cuda.empty_cache()
 
+    if "mid" in legs:
+        # forward of the 7B down-projection at a few hundred tokens (the split
+        # forward: one workgroup per rank and tile, then a reduce pass);
+        # weight sets rotate past the last-level cache
+        mk = mask_dev(H)
+        nsets = 6
+        Ws = [randn_bf16((T, KR, H), 0.02) for _ in range(nsets)]
+        mid = {}
+        for Mm in (64, 128, 256, 512):
+            Xs = [randn_bf16((T, Mm, KR)) for _ in range(nsets)]
+            outs = [torch.empty((T, Mm, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+            wsm = torch.zeros(max(1, ops.fwd_workspace_bytes(T, Mm, KR, H)), dtype=torch.uint8, device=dev)
+            idx = [0]
+
+            def callm():
+                i = idx[0] % nsets
+                idx[0] += 1
+                ops.rowpar_pcr_fwd(Xs[i], Ws[i], mk, out=outs[i], workspace=wsm)
+
+            t = time_call(callm, 30, warm=6)
+            flops = 2.0 * Mm * K * H
+            nbytes = 2.0 * (T * Mm * KR + T * KR * H + T * Mm * H)
+            roof_ms = max(flops / (PEAK_BF16_TFLOPS * 1e9), nbytes / (PEAK_HBM_GBS * 1e6))
+            mid[f"M{Mm}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(flops / (t * 1e-3) / 1e12, 1),
+                             "GB/s": round(nbytes / (t * 1e-3) / 1e9, 1), "frac_roof": round(roof_ms / t, 4)}
+            del Xs, outs
+        res["mid_tokens_fwd"] = mid
+        del Ws
+        torch.cuda.empty_cache()
+
     if "decode_out" in legs:
         # the attention out-projection (Kr = 512): 33.6 MB of weights; 16 sets
         # rotate (537 MB, beyond the last-level cache)
@@ -621,6 +652,7 @@ def main():
         "fwd_masks_ms": res.get("fwd_masks_ms"),
         "decode_down_proj": res.get("decode_down_proj"),
         "decode_out_proj": res.get("decode_out_proj"),
+        "mid_tokens_fwd": res.get("mid_tokens_fwd"),
         "payload_inplace_reduce": res.get("payload_inplace_reduce"),
         "copy": res.get("copy"),
         "src": src_hash(),

@@ -72,15 +72,25 @@ const char* caat_status_string(int status);
  *   out[t][:, c] = sum_u Y_u[:, c]     for c in S   (same value on every rank)
  *   out[t][:, c] = Y_t[:, c]           for c not in S
  * rounded once to bf16 (nearest even).  `out` must not overlap X, W or mask.
- * Decode-shaped calls (M <= 192, taken 32 tokens at a time, H <= 65536)
- * run a weight-streaming kernel that needs
- * caat_rowpar_pcr_fwd_workspace_bytes() bytes of workspace; other calls need
- * none (pass NULL, 0).  The workspace starts with a 2 KiB region of 32-bit
- * arrival counters (the same size and place for every shape) that must be
- * zero when a call starts; every call leaves them zero again, so zero a new
- * workspace once before its first use and it stays valid for calls of any
- * later shape.  The rest (fp32 partials of the synced channels, from byte
- * 2048 on) may hold anything.
+ * Three kernels serve it, by shape:
+ *   - M <= 32 (and, with T = 1, M <= 192, 32 tokens at a time; H <= 65536):
+ *     a weight-streaming kernel whose workgroups exchange fp32 partials of
+ *     the synced channels through the workspace;
+ *   - 33 <= M, T >= 2, while ceil(H/128) * ceil(M/64) <= 2 * T * ceil(Kr/64)
+ *     + 128: one workgroup per (rank, 128 channels, 64 tokens) writes fp32
+ *     products Y[T,M,H] into the workspace, and a streaming pass reduces
+ *     them into out (the synced sum is the ascending-rank fp32 sum of the
+ *     per-rank products);
+ *   - otherwise the fused tile kernel (each tile walks all T ranks), which
+ *     needs no workspace.
+ * caat_rowpar_pcr_fwd_workspace_bytes() gives the bytes a call needs (0:
+ * pass NULL, 0).  The workspace starts with a 2 KiB region of 32-bit arrival
+ * counters (the same size and place for every shape) that must be zero when
+ * a call starts; every call leaves them zero again, so zero a new workspace
+ * once before its first use and it stays valid for calls of any later
+ * shape.  The rest (from byte 2048 on) may hold anything.  Every path gives
+ * the same value up to fp32 summation order; for a given shape and workspace
+ * the bits are fixed.
  */
 int caat_rowpar_pcr_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out,
                         int T, int M, int Kr, int H,
@@ -91,18 +101,20 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  * caat_rowpar_pcr_fwd for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation and results, with no workspace argument.
- * Decode-shaped calls use a scratch area owned by the library instead, a
- * static device array of CAAT_NOALLOC_SCRATCH_BYTES (16 MiB) on each GPU,
- * held until the process ends; it serves calls whose
- * caat_rowpar_pcr_fwd_workspace_bytes() is at most that (e.g. T*H <= 131056
- * channels over all ranks); larger ones return CAAT_ERR_WORKSPACE before
- * anything is enqueued.  The scratch of the device current at the call is
+ * Calls that need a workspace use a scratch area owned by the library
+ * instead, a static device array of CAAT_NOALLOC_SCRATCH_BYTES (16 MiB) on
+ * each GPU, held until the process ends.  A split-path call whose fp32
+ * products would exceed it runs the path the shape would take without the
+ * split (chunked decode or fused tiles: the same value up to fp32 summation
+ * order); a decode call whose partials exceed it (e.g. T*H > 131056 channels
+ * over all ranks at M = 32) returns CAAT_ERR_WORKSPACE before anything is
+ * enqueued.  The scratch of the device current at the call is
  * used (`stream` must belong to it); its arrival counters are cleared by the
  * call itself (a small fill kernel, no memset).  Every call on one GPU shares
  * that GPU's scratch, so calls that may overlap on one GPU (different
  * streams, different threads) race and must be serialised by the caller.
- * Calls that need no scratch (M > 192, or H > 65536) behave exactly like
- * caat_rowpar_pcr_fwd.  Neither call allocates; this one calls no hipMalloc,
+ * Calls that need no workspace behave exactly like caat_rowpar_pcr_fwd, and
+ * so do the others whose workspace fits the scratch.  Neither call allocates; this one calls no hipMalloc,
  * hipFree or allocating library routine at all.  CAAT_ERR_LAUNCH also covers
  * a failed lookup of the scratch's device address.
  */

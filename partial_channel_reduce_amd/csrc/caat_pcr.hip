@@ -10,6 +10,7 @@
 #include "gemm_kernels.hpp"
 #include "norm_kernels.hpp"
 #include "reduce_kernels.hpp"
+#include "split_kernel.hpp"
 
 namespace {
 
@@ -167,6 +168,23 @@ static uint32_t reduce_groups(const dim3& grid, long long slice_bytes) {
   return grid.x % g == 0 ? g : 1u;
 }
 
+// Partial channel-reduce of fp32 y[T,M,H] into bf16 o (the split forward's
+// second pass).
+int launch_reduce_f32_bf16(const float* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, hipStream_t s) {
+  const long long mh = (long long)M * H;
+  const uint32_t nvec = (uint32_t)(mh / 4);
+  const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
+  const uint32_t hv = (uint32_t)(H / 4);
+  const uint32_t hf = reduce_groups(grid, mh * 4);
+  switch (T) {
+    case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
+    case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
+    case 8: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
+    default: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
+  }
+  return launched();
+}
+
 // bf16 partial channel-reduce of y[T,M,H] into o (o == y: in place).  With
 // tbits (the backward's G, out of place), wholly local tiles of channels are
 // skipped and wholly synced ones written to rank 0's slot only.
@@ -224,9 +242,41 @@ constexpr size_t kDecCounterBytes = (size_t)(kDecMaxH / kDecCols) * sizeof(int);
 static_assert(kDecCounterBytes % 256 == 0, "partials stay 256-byte aligned");
 static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 
-size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
-  if (check_dims(T, M, Kr, H) != CAAT_OK || !use_decode(M, H)) return 0;
+// Token counts between decode and full tiles: the rank walk split across
+// workgroups, one per (rank, 128-channel block, 64-token block), each
+// writing its rank's fp32 product tile into the workspace (after the decode
+// kernel's counter region, which this path leaves alone), then one
+// streaming pass forms the partial channel-reduce into out.
+// It pays while the fused kernel is short of tiles for the length of its
+// serial walk (T x ceil(Kr/64) chunks per tile): up to 2 x walk + 128 fused
+// tiles of 128 channels x 64 tokens.  Measured on MI355X (random S, fused ->
+// split, us), which this rule splits at ties:
+//   T=8 Kr=1376 H=4096 (walk 176): M = 128 / 256 / 512 / 768 / 1024:
+//       91 / 164 / 170 / 180 / 194 -> 37 / 68 / 103 / 141 / 191
+//   T=4 Kr=1376 H=4096 (88): M = 256: 73 -> 32; M = 1024 (512 tiles): 89 -> 100
+//   T=8 Kr=704 H=2048 (88): M = 512 / 1024: 71 / 75 -> 32 / 60
+//   T=8 Kr=512 H=4096 (64): M = 128 / 256 / 512: 54 / 55 / 63 -> 18 / 30 / 60
+//   T=8 Kr=384 H=768 (48): M = 256 / 1024 / 2048: 45 / 45 / 48 -> 13 / 24 / 36
+//   T=8 Kr=96 H=768 (16): M = 1024: 23 -> 21; M = 2048 (192 tiles): 23 -> 30
+constexpr int kSplitMinM = kDecMaxM + 1;
+static bool use_split(int T, int M, int Kr, int H) {
+  const long long tiles = (long long)((H + 127) / 128) * ((M + 63) / 64);
+  const long long walk = (long long)T * ((Kr + kBK - 1) / kBK);
+  return T >= 2 && M >= kSplitMinM && tiles <= 2 * walk + 128;
+}
+
+// Workspace of a forward with a mask; `split` = whether the split path may
+// be taken (the allocation-free entry point declines it when its fp32 tiles
+// would not fit the library's scratch array).
+static size_t fwd_need(int T, int M, int Kr, int H, bool split) {
+  if (split && use_split(T, M, Kr, H)) return kDecCounterBytes + round256((size_t)T * M * H * sizeof(float));
+  if (!use_decode(M, H)) return 0;
   return decode_counter_bytes(H) + round256((size_t)T * (M < kDecMaxM ? M : kDecMaxM) * H * sizeof(float));
+}
+
+size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
+  if (check_dims(T, M, Kr, H) != CAAT_OK) return 0;
+  return fwd_need(T, M, Kr, H, true);
 }
 
 }  // extern "C"
@@ -250,9 +300,17 @@ int fwd_check_args(const uint16_t* X, const uint16_t* W, const uint8_t* mask, co
 // kernel's arrival counters (kDecCounterBytes, zero on entry) and then its
 // fp32 partials; it is only touched for decode-shaped calls with a mask.
 int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
-               int H, void* workspace, hipStream_t s) {
+               int H, void* workspace, hipStream_t s, bool split = true) {
   if (M == 0) return CAAT_OK;
   if (!mask) workspace = nullptr;  // never touched without synced channels
+  if (split && use_split(T, M, Kr, H)) {
+    const int tm = (H + kSplitBM - 1) / kSplitBM, tn = (M + kSplitBN - 1) / kSplitBN;
+    float* Y = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kDecCounterBytes) : nullptr;
+    hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, kSplitBN, kSplitNW>), dim3(T * tm * tn),
+                       dim3(kSplitNW * 64), 0, s, X, W, out, Y, M, Kr, H, tm, tn);
+    if (int st = launched()) return st;
+    return Y ? launch_reduce_f32_bf16(Y, mask, out, T, M, H, s) : CAAT_OK;
+  }
   if (use_decode(M, H)) {
     // workspace: the per-block arrival counters, then the fp32 partials
     int* arrivals = static_cast<int*>(workspace);
@@ -361,7 +419,10 @@ int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint
                                 int M, int Kr, int H, void* stream) {
   if (!mask) return CAAT_ERR_NULL;
   if (int st = fwd_check_args(X, W, mask, out, T, M, Kr, H)) return st;
-  const size_t need = caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H);
+  // The split path's fp32 tiles may not fit the scratch array; such calls
+  // take the tiled or chunked decode path instead (no scratch, or a chunk's).
+  const bool split = fwd_need(T, M, Kr, H, true) <= kScratchBytes;
+  const size_t need = fwd_need(T, M, Kr, H, split);
   if (need > kScratchBytes) return CAAT_ERR_WORKSPACE;
   if (M == 0) return CAAT_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -375,7 +436,7 @@ int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint
                        static_cast<uint32_t*>(ws), nc, 0u);
     if (int st = launched()) return st;
   }
-  return fwd_launch(X, W, mask, out, T, M, Kr, H, ws, s);
+  return fwd_launch(X, W, mask, out, T, M, Kr, H, ws, s, split);
 }
 
 int caat_colpar_fwd(const uint16_t* A, const uint16_t* W, uint16_t* U, int T, int M, int K, int N, void* stream) {

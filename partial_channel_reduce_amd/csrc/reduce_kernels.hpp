@@ -97,6 +97,46 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
   }
 }
 
+// ---- fp32 in, bf16 out: the second pass of the split forward ----------------
+// out[t] = bf16 of the partial channel-reduce of the fp32 per-rank products
+// Y[T,M,H]: on synced channels the ascending-rank fp32 sum starting from rank
+// 0's value, elsewhere Y[t]; one thread per 4-channel vector, T 16-byte loads
+// and T 8-byte stores.
+template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
+__global__ void __launch_bounds__(kReduceThreads)
+pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
+                           int T_rt, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups) {
+  const int T = TC > 0 ? TC : T_rt;
+  constexpr int NR = TC > 0 ? TC : 1;  // ranks kept in registers
+  const uint32_t v = reduce_block(groups) * kReduceThreads + threadIdx.x;
+  if (v >= nvec) return;
+  const int c = (int)(v % hvec) * 4;
+  const long long base = (long long)v * 4;
+  const uint32_t mk = *reinterpret_cast<const uint32_t*>(mask + c);
+  const bool s0 = (mk & 0xffu) != 0, s1 = (mk & 0xff00u) != 0;
+  const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
+  f32x4 y[NR];
+  f32x4 s;
+  if (TC > 0) {
+#pragma unroll
+    for (int t = 0; t < NR; ++t) y[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + t * mh + base));
+    s = y[0];
+#pragma unroll
+    for (int t = 1; t < NR; ++t) s += y[t];
+  } else {
+    s = *reinterpret_cast<const f32x4*>(Y + base);
+    for (int t = 1; t < T; ++t) s += *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+  }
+#pragma unroll 8
+  for (int t = 0; t < T; ++t) {
+    const f32x4 yt = TC > 0 ? y[t < NR ? t : 0] : *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+    u32x2 o;
+    o[0] = pack_bf16x2(s0 ? s.x : yt.x, s1 ? s.y : yt.y);
+    o[1] = pack_bf16x2(s2 ? s.z : yt.z, s3 ? s.w : yt.w);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * mh + base));
+  }
+}
+
 // ---- classes of 256-channel tiles, for the backward's reduced gradient -------
 // With a contiguous sync set most tiles of channels are wholly synced or
 // wholly local.  Then the backward's G needs no per-rank copy there: a wholly

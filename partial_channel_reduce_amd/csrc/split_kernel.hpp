@@ -1,0 +1,118 @@
+// Forward for token counts between decode and full tiles (the rank walk
+// split across workgroups).
+//
+// The fused forward gives each (channel tile, token tile) to one workgroup,
+// which walks all T ranks' contractions in turn.  With a few hundred tokens
+// that leaves too few tiles to fill the chip, each with a long serial walk.
+// Here every (rank t, 128-channel block, 64-token block) is a workgroup of its
+// own and computes only Y_t's tile (the same copy and MFMA loop as the fused
+// forward, over rank t's contraction):
+//   * with no mask (the column-parallel layer: nothing synced) it writes the
+//     tile to out[t] in bf16;
+//   * otherwise it writes the fp32 tile to Y[t] in the workspace, and a
+//     second kernel, pcr_reduce_f32_bf16_kernel, forms the partial
+//     channel-reduce of Y into out: on synced channels the fp32 sum over the
+//     ranks in ascending order, starting from rank 0's value, rounded once
+//     (the same value on every rank); elsewhere the rank's own value.
+// Per-rank products are fp32 MFMA sums over that rank's contraction (CAAT-Net
+// paper, Introduction: only the channels of the sync set are reduced over the
+// tensor-parallel ranks).  The kernel boundary orders the two passes, so no
+// cross-workgroup handoff is needed: the fp32 tiles go out with plain stores,
+// and the four 16-byte stores that cover each 128-byte row piece merge into
+// whole lines in L2.
+#pragma once
+
+#include "gemm_core.hpp"
+
+namespace caat {
+
+constexpr int kSplitBM = 128;  // channels per workgroup
+constexpr int kSplitBN = 64;   // tokens per workgroup
+constexpr int kSplitNW = 4;
+
+template <int BM, int BN, int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
+rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
+                        float* __restrict__ Y, int M, int Kr, int H, int tiles_m, int tiles_n) {
+  using S = TileShape<BM, BN, NW>;
+  using RS = RowStage<S::WM>;
+  static_assert(NW * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / S::WGN, wn = wave % S::WGN;
+  const int per_rank = tiles_m * tiles_n;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = lin / per_rank;
+  const int tile = lin - t * per_rank;
+  int tm, tn;
+  tile_coords(tile, tiles_m, tiles_n, tm, tn);
+  const int c0 = tm * BM, m0 = tn * BN;  // channel block, token block
+  const int chw = c0 + wm * S::WM;       // this wave's first channel
+  const int tkw = m0 + wn * S::WN;       // this wave's first token
+  const int nk = (Kr + kBK - 1) / kBK;
+  const int kv_last = Kr - (nk - 1) * kBK;
+  const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
+
+  f32x16 acc[S::WI][S::WJ];
+  zero_acc<BM, BN, NW>(acc);
+  const MnDma<BM> da(W + t * KH, (uint32_t)(KH * 2), H, lane, wave);
+  const KcDma db(X + t * MK, (uint32_t)(MK * 2), Kr, lane, wave);
+  auto issue = [&](int c) {
+    uint16_t* buf = smem + (c & 1) * S::BUF;
+    da.template load<NW>(H, c0, c * kBK, buf, wave);
+    db.load<BN, NW>(Kr, m0, c * kBK, buf + BM * kBK, wave);
+  };
+  issue(0);
+  for (int c = 0; c < nk; ++c) {
+    uint16_t* As = smem + (c & 1) * S::BUF;
+    uint16_t* Bs = As + BM * kBK;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c == nk - 1 && kv_last < kBK) {  // X's columns past Kr: the next row's values
+      zero_kcont_tail<BN, S::THREADS>(Bs, kv_last, tid);
+      __syncthreads();
+    }
+    mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
+                          [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
+                          [&] {
+                            if (c + 1 < nk) issue(c + 1);
+                          });
+  }
+
+  __syncthreads();  // every wave is done with the operand buffers
+  if (Y == nullptr) {
+    // bf16 straight to out[t], staged through this wave's part of LDS and
+    // written as whole lines
+    uint16_t* st = smem + wave * (S::WM * S::WN);
+#pragma unroll
+    for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+      for (int j = 0; j < S::WJ; ++j) RS::put(st, acc[i][j], i, j * 32, lane);
+    lds_wave_sync();
+    uint16_t* ou = out + t * MH;
+    RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 w) {
+      const int tok = tkw + r, ch = chw + cc * 8;
+      if (tok < M && ch < H) st16_nt(ou + (long long)tok * H + ch, w);
+    });
+    return;
+  }
+  // fp32 to Y[t]: accumulator registers 4q..4q+3 of block (i, j) are 4
+  // consecutive channels of one token.
+  float* yt = Y + t * MH;
+#pragma unroll
+  for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+    for (int j = 0; j < S::WJ; ++j) {
+      const int tok = tkw + j * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ch = chw + i * 32 + q * 8 + (lane >> 5) * 4;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (tok < M && ch < H) *reinterpret_cast<f32x4*>(yt + (long long)tok * H + ch) = v;
+      }
+    }
+}
+
+}  // namespace caat
+

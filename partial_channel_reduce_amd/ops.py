@@ -122,8 +122,9 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """out[T,M,H] = partial channel-reduce of X[t] @ W[t] (see caat_pcr.h).
 
-    A caller-supplied `workspace` for decode-shaped calls (M <= 192) must be
-    zeroed once before its first use; the library leaves its counters zero."""
+    A caller-supplied `workspace` (fwd_workspace_bytes of it; shapes served by
+    the decode or split kernels need one) must be zeroed once before its first
+    use; the library leaves its counters zero."""
     _require(X, "X", torch.bfloat16, 3)
     dev = X.device
     _require(W, "W", torch.bfloat16, 3, dev)
@@ -139,7 +140,7 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
         raise ValueError(f"out must be {(T, M, H)}, got {tuple(out.shape)}")
     need = fwd_workspace_bytes(T, M, Kr, H)
     if workspace is None and need > 0:
-        # the decode kernel's arrival counters at its head must start at zero
+        # the arrival counters at its head must start at zero
         workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().caat_rowpar_pcr_fwd(_ptr(X), _ptr(W), _ptr(mask), _ptr(out), T, M, Kr, H, _ptr(workspace), ws_bytes,

@@ -119,15 +119,23 @@ def test_noalloc_fwd_validation(L):
 
 def test_workspace_sizes(L):
     T, Kr, H = 8, 1376, 4096
-    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 193, Kr, H) == 0  # tiled path needs none
+    # 33 .. 960 tokens at this width (at most 2 x 176 + 128 = 480 fused tiles
+    # of 128 x 64 for a walk of 8 x 22 chunks): the split forward's fp32
+    # products after the counter region
+    for M in (33, 100, 193, 960):
+        assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == 2048 + T * M * H * 4
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 961, Kr, H) == 0  # 512 tiles: fused, no workspace
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 512, 512, H) == 2048 + T * 512 * H * 4  # 256 tiles, walk 64
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 513, 512, H) == 0  # 288 tiles: fused
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(1, 100, Kr, H) == 2048 + 32 * H * 4  # one rank: chunked decode
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65536) == 2048 + 2 * 8 * 65536 * 4
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65544) == 0  # above 65536 channels: tiled
     for M in (1, 8, 32):
         need = L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H)
         assert need == 2048 + T * M * H * 4  # fixed arrival-counter region + fp32 partials
-    # 33 .. 192 tokens run 32 at a time and share one chunk's partials
+    # with one rank, 33 .. 192 tokens run 32 at a time and share one chunk's partials
     for M in (33, 100, 192):
-        assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == L.caat_rowpar_pcr_fwd_workspace_bytes(T, 32, Kr, H)
+        assert L.caat_rowpar_pcr_fwd_workspace_bytes(1, M, Kr, H) == L.caat_rowpar_pcr_fwd_workspace_bytes(1, 32, Kr, H)
     assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) >= T * 16384 * H * 2  # G for every rank
     assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) % 256 == 0
     assert L.caat_pcr_bwd_workspace_bytes(T, 0, Kr, H) == 0

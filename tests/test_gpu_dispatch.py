@@ -41,16 +41,19 @@ def _tiles(rows, cols, tr, tc, batch=1):
     return -(-rows // tr) * -(-cols // tc) * batch
 
 
-# Forward, H = 1024 channels (8 tiles of 128, 4 of 256):
-#   M <= 192 decode;  M = 193 the first 128x64-tile call;
+# Forward, T = 2 ranks, Kr = 40, H = 1024 channels (8 tiles of 128, 4 of 256):
+#   M <= 32 decode;  33 <= M <= 1024 the split forward (at most 2 x 2 + 128
+#   fused tiles of 128x64 for a walk of two chunks);  M = 1025 the first
+#   128x64-tile call;
 #   M = 8064 -> 504 tiles of 128x128 (still 128x64), M = 8065 -> 512 (128x128);
 #   M = 16128 -> 252 tiles of 256x256 (still 128x128), M = 16129 -> 256 (256x256).
-FWD_M = [192, 193, 8064, 8065, 16128, 16129]
+FWD_M = [32, 33, 192, 1024, 1025, 8064, 8065, 16128, 16129]
 
 
 @pytest.mark.parametrize("M", FWD_M)
 def test_fwd_across_kernel_switch(ops, M):
     T, Kr, H = 2, 40, 1024
+    assert _tiles(H, 1024, 128, 64) == 128 and _tiles(H, 1025, 128, 64) == 136
     assert _tiles(8064, H, 128, 128) == 504 and _tiles(8065, H, 128, 128) == 512
     assert _tiles(16128, H, 256, 256) == 252 and _tiles(16129, H, 256, 256) == 256
     _announce(f"dispatch fwd T={T} M={M} Kr={Kr} H={H}")
