@@ -76,8 +76,11 @@ const char* caat_status_string(int status);
  *   - M <= 32 (and, with T = 1, M <= 192, 32 tokens at a time; H <= 65536):
  *     a weight-streaming kernel whose workgroups exchange fp32 partials of
  *     the synced channels through the workspace;
- *   - 33 <= M, T >= 2, while ceil(H/128) * ceil(M/64) <= 2 * T * ceil(Kr/64)
- *     + 128: one workgroup per (rank, 128 channels, 64 tokens) writes fp32
+ *   - 33 <= M, T >= 2, while the fused kernel below would have few tiles for
+ *     its walk over the ranks (ceil(H/128) * ceil(M/64) at most
+ *     3 * T * ceil(Kr/64) + 128 with T <= 8, 2 * T * ceil(Kr/64) + 64 with
+ *     more, 128 when Kr <= 128): one workgroup per (rank, 128 channels, 64
+ *     or 128 tokens) writes fp32
  *     products Y[T,M,H] into the workspace, and a streaming pass reduces
  *     them into out (the synced sum is the ascending-rank fp32 sum of the
  *     per-rank products);

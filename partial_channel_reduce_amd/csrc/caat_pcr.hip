@@ -247,22 +247,28 @@ static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 // writing its rank's fp32 product tile into the workspace (after the decode
 // kernel's counter region, which this path leaves alone), then one
 // streaming pass forms the partial channel-reduce into out.
-// It pays while the fused kernel is short of tiles for the length of its
-// serial walk (T x ceil(Kr/64) chunks per tile): up to 2 x walk + 128 fused
-// tiles of 128 channels x 64 tokens.  Measured on MI355X (random S, fused ->
-// split, us), which this rule splits at ties:
-//   T=8 Kr=1376 H=4096 (walk 176): M = 128 / 256 / 512 / 768 / 1024:
-//       91 / 164 / 170 / 180 / 194 -> 37 / 68 / 103 / 141 / 191
-//   T=4 Kr=1376 H=4096 (88): M = 256: 73 -> 32; M = 1024 (512 tiles): 89 -> 100
-//   T=8 Kr=704 H=2048 (88): M = 512 / 1024: 71 / 75 -> 32 / 60
-//   T=8 Kr=512 H=4096 (64): M = 128 / 256 / 512: 54 / 55 / 63 -> 18 / 30 / 60
-//   T=8 Kr=384 H=768 (48): M = 256 / 1024 / 2048: 45 / 45 / 48 -> 13 / 24 / 36
-//   T=8 Kr=96 H=768 (16): M = 1024: 23 -> 21; M = 2048 (192 tiles): 23 -> 30
+// It pays while the fused kernel is short of tiles (of 128 channels x 64
+// tokens) for the length of its serial walk, walk = T x ceil(Kr/64) chunks:
+// up to 3 x walk + 128 tiles with T <= 8, 2 x walk + 64 with more ranks (the
+// second pass reads T ranks' fp32 products), and only up to 128 tiles when
+// each rank's contraction is at most two chunks (the fused kernel then holds
+// the ranks' tiles in registers).  Measured on MI355X (random S, fused ->
+// split, us):
+//   T=8  Kr=1376 H=4096 (walk 176): M = 128 / 256 / 512 / 1024 / 1280 / 1536:
+//        91 / 164 / 170 / 196 / 220 / 238 -> 37 / 47 / 90 / 165 / 194 / 236
+//        (M = 1664: 357 -> 254, past the rule: the fused kernel's second round)
+//   T=4  Kr=1376 H=4096 (88): M = 256 / 512 / 768 / 960: 73 / 80 / 82 / 83 -> 32 / 45 / 66 / 77
+//   T=8  Kr=704  H=2048 (88): M = 512 / 1024 / 1536 / 1920: 71 / 75 / 85 / 113 -> 31 / 55 / 78 / 100
+//   T=8  Kr=512  H=4096 (64): M = 256 / 512 / 640 / 768: 55 / 60 / 67 / 69 -> 26 / 54 / 61 / 72
+//   T=8  Kr=384  H=768  (48): M = 1024 / 2304 / 3328: 45 / 50 / 58 -> 24 / 40 / 50
+//   T=8  Kr=96   H=768  (16): M = 1024 / 1600: 23 / 23 -> 21 / 29
+//   T=16 Kr=688  H=4096 (176): M = 256 / 512 / 960: 178 / 193 / 230 -> 87 / 148 / 242
 constexpr int kSplitMinM = kDecMaxM + 1;
 static bool use_split(int T, int M, int Kr, int H) {
   const long long tiles = (long long)((H + 127) / 128) * ((M + 63) / 64);
-  const long long walk = (long long)T * ((Kr + kBK - 1) / kBK);
-  return T >= 2 && M >= kSplitMinM && tiles <= 2 * walk + 128;
+  const long long nk = (Kr + kBK - 1) / kBK, walk = (long long)T * nk;
+  const long long limit = nk <= 2 ? 128 : T <= 8 ? 3 * walk + 128 : 2 * walk + 64;
+  return T >= 2 && M >= kSplitMinM && tiles <= limit;
 }
 
 // Workspace of a forward with a mask; `split` = whether the split path may
@@ -304,10 +310,21 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   if (M == 0) return CAAT_OK;
   if (!mask) workspace = nullptr;  // never touched without synced channels
   if (split && use_split(T, M, Kr, H)) {
-    const int tm = (H + kSplitBM - 1) / kSplitBM, tn = (M + kSplitBN - 1) / kSplitBN;
     float* Y = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kDecCounterBytes) : nullptr;
-    hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, kSplitBN, kSplitNW>), dim3(T * tm * tn),
-                       dim3(kSplitNW * 64), 0, s, X, W, out, Y, M, Kr, H, tm, tn);
+    // 128-token tiles once they still give two workgroups per CU (at
+    // T = 8, H = 4096, M = 256 / 512 / 768: 68 / 100 / 138 -> 47 / 90 /
+    // 120 us), else 64-token ones (M = 128 there: 36 against 38 us).
+    const int tm = (H + kSplitBM - 1) / kSplitBM;
+    const long long wg128 = (long long)T * tm * ((M + 127) / 128);
+    if (wg128 >= 512) {
+      const int tn = (M + 127) / 128;
+      hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 128, kSplitNW>), dim3(T * tm * tn), dim3(kSplitNW * 64), 0,
+                         s, X, W, out, Y, M, Kr, H, tm, tn);
+    } else {
+      const int tn = (M + 63) / 64;
+      hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 64, kSplitNW>), dim3(T * tm * tn), dim3(kSplitNW * 64), 0,
+                         s, X, W, out, Y, M, Kr, H, tm, tn);
+    }
     if (int st = launched()) return st;
     return Y ? launch_reduce_f32_bf16(Y, mask, out, T, M, H, s) : CAAT_OK;
   }

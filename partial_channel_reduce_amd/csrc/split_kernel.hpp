@@ -4,7 +4,7 @@
 // The fused forward gives each (channel tile, token tile) to one workgroup,
 // which walks all T ranks' contractions in turn.  With a few hundred tokens
 // that leaves too few tiles to fill the chip, each with a long serial walk.
-// Here every (rank t, 128-channel block, 64-token block) is a workgroup of its
+// Here every (rank t, 128-channel block, 64- or 128-token block) is a workgroup of its
 // own and computes only Y_t's tile (the same copy and MFMA loop as the fused
 // forward, over rank t's contraction):
 //   * with no mask (the column-parallel layer: nothing synced) it writes the
@@ -26,8 +26,8 @@
 
 namespace caat {
 
-constexpr int kSplitBM = 128;  // channels per workgroup
-constexpr int kSplitBN = 64;   // tokens per workgroup
+// Tiles: 128 channels x 64 or 128 tokens, four waves.
+constexpr int kSplitBM = 128;
 constexpr int kSplitNW = 4;
 
 template <int BM, int BN, int NW>

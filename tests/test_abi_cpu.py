@@ -119,14 +119,18 @@ def test_noalloc_fwd_validation(L):
 
 def test_workspace_sizes(L):
     T, Kr, H = 8, 1376, 4096
-    # 33 .. 960 tokens at this width (at most 2 x 176 + 128 = 480 fused tiles
-    # of 128 x 64 for a walk of 8 x 22 chunks): the split forward's fp32
-    # products after the counter region
-    for M in (33, 100, 193, 960):
+    # 33 .. 1280 tokens at this width (at most 3 x 176 + 128 = 656 fused
+    # tiles of 128 x 64 for a walk of 8 x 22 chunks): the split forward's
+    # fp32 products after the counter region
+    for M in (33, 100, 193, 1280):
         assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == 2048 + T * M * H * 4
-    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 961, Kr, H) == 0  # 512 tiles: fused, no workspace
-    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 512, 512, H) == 2048 + T * 512 * H * 4  # 256 tiles, walk 64
-    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 513, 512, H) == 0  # 288 tiles: fused
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 1281, Kr, H) == 0  # 672 tiles: fused, no workspace
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 640, 512, H) == 2048 + T * 640 * H * 4  # 320 tiles, walk 64
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 641, 512, H) == 0  # 352 tiles: fused
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(16, 832, 688, H) == 2048 + 16 * 832 * H * 4  # 416 = 2 x 176 + 64
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(16, 833, 688, H) == 0
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 256, 96, 768) == 2048 + T * 256 * 768 * 4  # 24 tiles
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 1408, 96, 768) == 0  # 132 tiles, two-chunk walk: fused
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(1, 100, Kr, H) == 2048 + 32 * H * 4  # one rank: chunked decode
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65536) == 2048 + 2 * 8 * 65536 * 4
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65544) == 0  # above 65536 channels: tiled

@@ -28,8 +28,10 @@ def _announce(msg):
 
 
 # (T, Kr): held in registers for T <= 4 and for (5..8, Kr <= 128); the
-# standard kernel for (5, 136) and (8, 136).  M = 1000 and H = 776 leave a
-# partial token tile and a partial channel tile (776 = 6 x 128 + 8).
+# standard kernel for (5, 136) and (8, 136).  M = 3600 and H = 776 leave a
+# partial token tile and a partial channel tile (776 = 6 x 128 + 8); 399
+# fused tiles of 128 x 64 are more than the split forward takes for any of
+# these walks, and fewer than 512 of 128 x 128, so the 128 x 64 path runs.
 RANKS_KR = [(2, 40), (3, 136), (4, 384), (4, 1376), (5, 128), (8, 96), (8, 8), (5, 136), (8, 136)]
 MASKS = [("random", 0.5), ("prefix", 0.5), ("strided", 0.5), ("random", 0.0), ("random", 1.0), ("random", 0.1)]
 
@@ -37,7 +39,7 @@ MASKS = [("random", 0.5), ("prefix", 0.5), ("strided", 0.5), ("random", 0.0), ("
 @pytest.mark.parametrize("T,Kr", RANKS_KR)
 @pytest.mark.parametrize("kind,p", MASKS)
 def test_fwd_rank_queue_bitwise(ops, T, Kr, kind, p):
-    M, H = 1000, 776
+    M, H = 3600, 776
     _announce(f"fwd rank queue T={T} M={M} Kr={Kr} H={H} {kind} p={p}")
     zf = 0.4 if T * Kr <= 1200 else 0.97
     X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=T * 100 + Kr, lo=-1, hi=1, x_zero_frac=zf)
