@@ -83,6 +83,23 @@ def test_dx_across_kernel_switch(ops, M):
     assert np.array_equal(G.from_dev_bf16(dXd), rdX)
 
 
+# dX with 256 big tiles (T = 8, M = 8192: 32 token tiles): Kr = 248 fills
+# under a 256-row tile, so the 128x128 kernel runs; Kr = 256 the 256x256 one.
+@pytest.mark.parametrize("Kr", [248, 256])
+def test_dx_short_contraction_switch(ops, Kr):
+    T, M, H = 8, 8192, 64
+    assert _tiles(M, Kr, 256, 256, T) == 256
+    _announce(f"dispatch dX short Kr T={T} M={M} Kr={Kr} H={H}")
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=Kr, lo=-1, hi=1, x_zero_frac=0.5)
+    dZ = _int_grad(T, M, H, Kr)
+    mask = synth.make_mask(H, 0.5, "random", seed=Kr + 4)
+    rdX, _ = oracle.pcr_bwd(dZ, X, W, mask)
+    assert np.abs(rdX).max() <= 256
+    dXd, _ = ops.pcr_bwd(G.to_dev_bf16(dZ), G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), need_dw=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(dXd), rdX)
+
+
 # dW = X^T G, T = 4, Kr = 264 (2 row tiles of 256): H = 7936 -> 31 channel
 # tiles, 248 big tiles (128x128 kernel); H = 7944 -> 32, 256 (256x256).
 @pytest.mark.parametrize("H", [7936, 7944])

@@ -2,9 +2,10 @@
 nothing, so its calls run on any stream and can be captured into a HIP graph
 (the decode kernel's arrival counters return to zero after every call).
 Checked here: a side stream gives the default stream's bits; a captured
-sequence (decode-shaped forward, tiled forward, backward) replayed several
-times, with eager calls and synchronisation in between, reproduces the eager
-results bit for bit every time."""
+sequence (decode-shaped forward, split forward and its reduce pass, fused
+tiled forward, backward) replayed several times, with eager calls and
+synchronisation in between, reproduces the eager results bit for bit every
+time."""
 import numpy as np
 import pytest
 import torch
@@ -57,22 +58,30 @@ def test_graph_replays_match_eager(ops):
     Xt_, _ = synth.make_fwd_inputs(T, Mt, Kr, H, seed=53)
     dZ_ = synth.make_grad(T, Mt, H, seed=53)
     Xdec, W, Xt, dZ = G.to_dev_bf16(Xd_), G.to_dev_bf16(W_), G.to_dev_bf16(Xt_), G.to_dev_bf16(dZ_)
+    # a fused-tile forward too: 2100 tokens with a two-chunk contraction
+    Mf, Krf = 2100, 96
+    Xf_, Wf_ = synth.make_fwd_inputs(T, Mf, Krf, H, seed=54)
+    Xf, Wf = G.to_dev_bf16(Xf_), G.to_dev_bf16(Wf_)
+    assert ops.fwd_workspace_bytes(T, Mf, Krf, H) == 0 and ops.fwd_workspace_bytes(T, Mt, Kr, H) > 2048
     # every buffer exists before capture: nothing is allocated inside the graph
     o_dec = torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev)
     o_t = torch.empty((T, Mt, H), dtype=torch.bfloat16, device=dev)
+    o_f = torch.empty((T, Mf, H), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((T, Mt, Kr), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((T, Kr, H), dtype=torch.bfloat16, device=dev)
     ws_dec = torch.zeros(ops.fwd_workspace_bytes(T, Md, Kr, H), dtype=torch.uint8, device=dev)
+    ws_t = torch.zeros(ops.fwd_workspace_bytes(T, Mt, Kr, H), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(ops.bwd_workspace_bytes(T, Mt, Kr, H), dtype=torch.uint8, device=dev)
 
     def seq():
         ops.rowpar_pcr_fwd(Xdec, W, mask, out=o_dec, workspace=ws_dec)
-        ops.rowpar_pcr_fwd(Xt, W, mask, out=o_t)
+        ops.rowpar_pcr_fwd(Xt, W, mask, out=o_t, workspace=ws_t)  # split forward + reduce pass
+        ops.rowpar_pcr_fwd(Xf, Wf, mask, out=o_f)  # fused tiles, no workspace
         ops.pcr_bwd(dZ, Xt, W, mask, dX=dX, dW=dW, workspace=ws_bwd)
 
     seq()
     torch.cuda.synchronize()
-    want = [t.clone() for t in (o_dec, o_t, dX, dW)]
+    want = [t.clone() for t in (o_dec, o_t, o_f, dX, dW)]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -87,11 +96,11 @@ def test_graph_replays_match_eager(ops):
 
     scratch = torch.empty_like(o_t)
     for rep in range(4):
-        for t in (o_dec, o_t, dX, dW):
+        for t in (o_dec, o_t, o_f, dX, dW):
             t.fill_(0)
         g.replay()
         torch.cuda.synchronize()
-        for name, got, ref in zip(("decode out", "out", "dX", "dW"), (o_dec, o_t, dX, dW), want):
+        for name, got, ref in zip(("decode out", "split out", "fused out", "dX", "dW"), (o_dec, o_t, o_f, dX, dW), want):
             assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), (rep, name)
         # eager work between replays, on other buffers
         ops.rowpar_pcr_fwd(Xt, W, mask, out=scratch)
