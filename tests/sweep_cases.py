@@ -1,0 +1,45 @@
+"""Seeded random shapes for the GPU sweep test, with the forward path each
+one takes (mirroring the library's dispatch rules, so the sweep can assert
+that every path is covered)."""
+import numpy as np
+
+
+def forward_path(T, M, Kr, H):
+    """Which forward kernel the library runs for (T, M, Kr, H) with a mask."""
+    if M <= 32 and H <= 65536:
+        return "decode"
+    tiles64 = -(-H // 128) * -(-M // 64)
+    nk = -(-Kr // 64)
+    walk = T * nk
+    limit = 128 if nk <= 2 else (3 * walk + 128 if T <= 8 else 2 * walk + 64)
+    if T >= 2 and tiles64 <= limit:
+        return "split128" if T * -(-H // 128) * -(-M // 128) >= 512 else "split64"
+    if M <= 192 and H <= 65536:
+        return "chunked"
+    if -(-M // 256) * -(-H // 256) >= 256:
+        return "fused256"
+    if -(-H // 128) * -(-M // 128) < 512:
+        return "queue" if T >= 2 and (T <= 4 or (T <= 8 and Kr <= 128)) else "fused128x64"
+    return "fused128"
+
+
+def cases(n=64, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    kinds = [("random", 0.5), ("prefix", 0.5), ("strided", 0.5), ("random", 0.3), ("random", 0.0), ("random", 1.0)]
+    while len(out) < n:
+        T = int(rng.choice([1, 2, 3, 4, 5, 8, 8, 8, 13, 16]))
+        M = int(rng.choice([1, 5, 17, 32, 33, 64, 100, 150, 193, 300, 700, 1000, 1500, 2100, 3000]))
+        Kr = 8 * int(rng.integers(1, 200))
+        H = 8 * int(rng.integers(1, 280))
+        if T * M * Kr * H > 3e8:  # keep the fp64 oracle quick
+            continue
+        kind, p = kinds[int(rng.integers(len(kinds)))]
+        out.append((T, M, Kr, H, kind, p, int(rng.integers(1 << 30))))
+    # paths that need more tiles than the size cap usually allows: split with
+    # 128-token tiles, fused 128x128 and 256x256 tiles, more register-queue
+    # and fused 128x64 tiles
+    out += [(8, 512, 192, 2048, "random", 0.5, 11), (2, 4096, 16, 2048, "strided", 0.5, 12),
+            (2, 8192, 8, 2048, "random", 0.5, 13), (4, 3000, 40, 776, "prefix", 0.5, 14),
+            (8, 3000, 96, 512, "random", 0.5, 15), (5, 2500, 200, 264, "random", 0.5, 16)]
+    return out

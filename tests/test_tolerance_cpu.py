@@ -103,3 +103,11 @@ def test_g_rounding_allowance():
     ts, ms, ks = np.array([1, 0, 7]), np.array([5, 0, 7]), np.array([3, 1375, 700])
     assert np.allclose(G.dx_rows_g_allowance(dZ, W, mask, ts, ms), ax[ts, ms])
     assert np.allclose(G.dw_rows_g_allowance(dZ, X, mask, ts, ks, block=3), aw[ts, ks])
+
+
+def test_sweep_covers_every_forward_path():
+    """The GPU sweep's seeded shapes reach every forward kernel."""
+    from tests.sweep_cases import cases, forward_path
+
+    paths = {forward_path(*c[:4]) for c in cases()}
+    assert paths >= {"decode", "chunked", "split64", "split128", "fused128x64", "fused128", "fused256", "queue"}, paths
