@@ -41,5 +41,8 @@ def cases(n=64, seed=2026):
     # and fused 128x64 tiles
     out += [(8, 512, 192, 2048, "random", 0.5, 11), (2, 4096, 16, 2048, "strided", 0.5, 12),
             (2, 8192, 8, 2048, "random", 0.5, 13), (4, 3000, 40, 776, "prefix", 0.5, 14),
-            (8, 3000, 96, 512, "random", 0.5, 15), (5, 2500, 200, 264, "random", 0.5, 16)]
+            (8, 3000, 96, 512, "random", 0.5, 15), (5, 2500, 200, 264, "random", 0.5, 16),
+            # the largest rank count the library takes
+            (64, 20, 16, 264, "random", 0.5, 17), (64, 100, 72, 128, "strided", 0.5, 18),
+            (64, 900, 8, 64, "random", 0.5, 19), (64, 8256, 8, 64, "prefix", 0.5, 20)]
     return out

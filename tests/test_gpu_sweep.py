@@ -45,7 +45,10 @@ def test_sweep_forward_bitwise(ops, case):
     assert np.array_equal(G.from_dev_bf16(out), ref)
 
 
-@pytest.mark.parametrize("case", CASES[::4], ids=[f"T{c[0]}-M{c[1]}-Kr{c[2]}-H{c[3]}-{c[4]}{c[5]}" for c in CASES[::4]])
+BWD_CASES = CASES[::4] + [c for c in CASES if c[0] == 64 and c not in CASES[::4]]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"T{c[0]}-M{c[1]}-Kr{c[2]}-H{c[3]}-{c[4]}{c[5]}" for c in BWD_CASES])
 def test_sweep_backward_bitwise(ops, case):
     T, M, Kr, H, kind, p, seed = case
     print(f"[case] sweep bwd {case}", flush=True)
