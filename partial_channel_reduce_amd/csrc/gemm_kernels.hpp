@@ -243,10 +243,14 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 // channels), and small contractions lose the per-rank drains.  The queue
 // shifts by one slot per rank (static register indices), so the rank loop
 // needs no unrolling.  It costs (T-1) x 16 registers per 32x32 block: with
-// a 128x64 tile, T <= 4 keeps three workgroups per CU, T <= 8 only one.
+// a 128x64 tile, T <= 4 keeps three workgroups per CU, T <= 8 two.
 // ============================================================================
+// (With TB = 8 the compiler is held to two workgroups per CU: a few rarely
+// touched values then live in scratch, and the second workgroup hides the
+// first one's latency -- T = 8, M = 8192, H = 768, Kr = 96: 67 -> 47 us, the
+// same bits.)
 template <int BM, int BN, int NW, int TB>
-__global__ void __launch_bounds__(NW * 64, 1)
+__global__ void __launch_bounds__(NW * 64, TB > 4 ? 2 : 1)
 rowpar_pcr_fwd_rb_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out, int T, int M, int Kr, int H,
                          int tiles_m, int tiles_n) {
