@@ -159,12 +159,29 @@ int launch_dw_split(const uint16_t* G, const uint16_t* X, uint16_t* dW, int T, i
 }
 
 // Last argument of the reduce kernels: how many row regions consecutive
-// workgroups alternate between -- 8 when the rank slices are a multiple of
-// 128 MiB apart, 2 when a multiple of 16 MiB, else 1 (the grid must divide).
-// (Measured on bf16 [T,16384,4096], 128 MiB slices: T = 16, 992 -> 892 us
-// with 8 regions instead of 2; T = 8, 381 vs 385 us.)
-static uint32_t reduce_groups(const dim3& grid, long long slice_bytes) {
-  const uint32_t g = slice_bytes % (128ll << 20) == 0 ? 8u : slice_bytes % (16ll << 20) == 0 ? 2u : 1u;
+// workgroups alternate between.  How much the T slices (slice_bytes apart)
+// camp on the same HBM channels depends on where the input and the output
+// sit in physical memory, which the virtual addresses do not show (the same
+// addresses ran at 753 and at 803 us in two processes).  The counts below
+// are the ones measured best over twelve placements of Y and out (offsets
+// of 0 to 256 MiB and of 4 KiB between them) on [T,16384,4096]:
+//   T <= 8, 256 MiB slices (fp32): 16 regions 751-804 us, 2: 764-793,
+//          8: 747-882, 4: 770-942, 32: 772-794;
+//   T <= 8, 128 MiB slices (bf16): 2 regions 374-384 us, 8: 388-414,
+//          16: 390-405;
+//   T = 16 (the runtime-T kernel), 128 MiB: 8 regions 887-904 us (16:
+//          927-974, 2: 932-998); 256 MiB: 8 regions 1758-1876 us (16:
+//          1816-1906, 2: 1829-1907).
+// Other spacings: 2 regions for multiples of 16 MiB, else none (the grid
+// must divide).  The region count changes no result, only the order in
+// which workgroups take the rows.
+static uint32_t reduce_groups(const dim3& grid, long long slice_bytes, int T) {
+  const long long MiB = 1ll << 20;
+  uint32_t g = 1u;
+  if (T > 8)
+    g = slice_bytes % (128 * MiB) == 0 ? 8u : slice_bytes % (16 * MiB) == 0 ? 2u : 1u;
+  else
+    g = slice_bytes % (256 * MiB) == 0 ? 16u : slice_bytes % (16 * MiB) == 0 ? 2u : 1u;
   return grid.x % g == 0 ? g : 1u;
 }
 
@@ -175,7 +192,7 @@ int launch_reduce_f32_bf16(const float* y, const uint8_t* mask, uint16_t* o, int
   const uint32_t nvec = (uint32_t)(mh / 4);
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
   const uint32_t hv = (uint32_t)(H / 4);
-  const uint32_t hf = reduce_groups(grid, mh * 4);
+  const uint32_t hf = reduce_groups(grid, mh * 4, T);
   switch (T) {
     case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
     case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
@@ -195,7 +212,7 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
   const int ip = (y == o) ? 1 : 0;
   const uint32_t hv = (uint32_t)(H / 8);
-  const uint32_t hf = reduce_groups(grid, mh * 2);
+  const uint32_t hf = reduce_groups(grid, mh * 2, T);
   switch (T) {
     case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
     case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
@@ -595,7 +612,7 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
     float* o = static_cast<float*>(out);
     const int ip = inplace ? 1 : 0;
     const uint32_t hv = (uint32_t)(H / 4);
-    const uint32_t hf = reduce_groups(grid, mh * 4);
+    const uint32_t hf = reduce_groups(grid, mh * 4, T);
     switch (T) {
       case 1: hipLaunchKernelGGL(pcr_reduce_f32_kernel<1>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
       case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
