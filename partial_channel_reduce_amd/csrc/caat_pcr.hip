@@ -682,8 +682,12 @@ int caat_partial_channel_reduce_residual_rmsnorm(const uint16_t* Y, const uint8_
   const long long mh = (long long)M * H;
   const int hv = H / 8;
   const int kv = hv <= kNormThreads ? 1 : hv <= 2 * kNormThreads ? 2 : 4;
+  // The T rank slices camp on HBM channels as in the reduce.  With T <= 8
+  // the reduce's region count (2 at 128 MiB slices: [8,16384,4096], 795-805
+  // -> 780-794 us, same bits; 8 regions: 891-894); plain order otherwise.
+  const uint32_t groups = T <= 8 ? reduce_groups(grid, mh * 2, T) : 1u;
 #define CAAT_RRN(KV, TC) \
-  hipLaunchKernelGGL((pcr_reduce_residual_rmsnorm_kernel<KV, TC>), grid, block, 0, s, Y, mask, R, gamma, Rout, N, T, H, mh, eps)
+  hipLaunchKernelGGL((pcr_reduce_residual_rmsnorm_kernel<KV, TC>), grid, block, 0, s, Y, mask, R, gamma, Rout, N, T, H, mh, eps, groups)
   if (kv == 1) {
     switch (T) {
       case 1: CAAT_RRN(1, 1); break;

@@ -88,12 +88,15 @@ template <int KV, int TC>
 __global__ void __launch_bounds__(kNormThreads)
 pcr_reduce_residual_rmsnorm_kernel(const uint16_t* __restrict__ Y, const uint8_t* __restrict__ mask,
                                    const uint16_t* R, const uint16_t* __restrict__ gamma, uint16_t* Rout,
-                                   uint16_t* __restrict__ N, int T_rt, int H, long long mh, float eps) {
+                                   uint16_t* __restrict__ N, int T_rt, int H, long long mh, float eps,
+                                   uint32_t groups) {
   constexpr int G = TC > 0 ? TC : 4;  // ranks normalised together
   const int T = TC > 0 ? TC : T_rt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hv = H / 8;
-  const long long row = (long long)blockIdx.x * H;  // token row m in every rank slice
+  // token row m in every rank slice (rows taken from `groups` regions in
+  // turn, as in the reduce kernels)
+  const long long row = (long long)reduce_block(groups) * H;
   __shared__ float wsum[kNormThreads / 64][G];
   u32x4 sel[KV], sv[KV];
   u32x4 yk[TC > 0 ? TC : 1][KV];
