@@ -66,8 +66,12 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = (H + kDecCols - 1) / kDecCols;
-  const int t = blockIdx.x / nb;
-  const int n0 = (blockIdx.x - t * nb) * kDecCols;
+  // Each XCD takes a contiguous range of (rank, channel block) items, so with
+  // T = 8 every XCD serves one rank and its L2 reads that rank's tokens once
+  // (numbered rank-major, each rank's blocks would be spread over all eight).
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = lin / nb;
+  const int n0 = (lin - t * nb) * kDecCols;
   const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
 
   // This wave's share of the contraction: 32-row stages wave, wave + 4,
@@ -248,7 +252,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   __shared__ int is_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const int blk = blockIdx.x - t * nb;
+  const int blk = lin - t * nb;
   if (tid == 0) is_last = __hip_atomic_fetch_add(arrivals + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == T - 1;
   __syncthreads();
   if (!is_last) return;
