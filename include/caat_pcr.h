@@ -79,8 +79,9 @@ const char* caat_status_string(int status);
  *   - 33 <= M, T >= 2, while the fused kernel below would have few tiles for
  *     its walk over the ranks (ceil(H/128) * ceil(M/64) at most
  *     3 * T * ceil(Kr/64) + 128 with T <= 8, 2 * T * ceil(Kr/64) + 64 with
- *     more, 128 when Kr <= 128): one workgroup per (rank, 128 channels, 64
- *     or 128 tokens) writes fp32
+ *     more, 128 when Kr <= 128): one workgroup per (rank, 128 channels x 64
+ *     or 128 tokens, or 256 x 256 when those fill whole rounds of the 256
+ *     CUs) writes fp32
  *     products Y[T,M,H] into the workspace, and a streaming pass reduces
  *     them into out (the synced sum is the ascending-rank fp32 sum of the
  *     per-rank products);

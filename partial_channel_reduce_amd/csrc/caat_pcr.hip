@@ -46,6 +46,9 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // MFMAs; the 128x128 tiles of small problems keep four.
 constexpr int kBigTileWaves = 8;
 
+// Compute units of the MI355X: one round of one-per-CU workgroups.
+constexpr int kCUs = 256;
+
 // 256 x 256 tiles (eight waves) when there are at least as many as CUs,
 // else 128 x 128 (four waves).  (At 256 to 511 big tiles, e.g. the weight
 // gradient of a 512-row out-projection shard, one big tile per CU beats four
@@ -328,12 +331,28 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   if (!mask) workspace = nullptr;  // never touched without synced channels
   if (split && use_split(T, M, Kr, H)) {
     float* Y = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kDecCounterBytes) : nullptr;
-    // 128-token tiles once they still give two workgroups per CU (at
-    // T = 8, H = 4096, M = 256 / 512 / 768: 68 / 100 / 138 -> 47 / 90 /
-    // 120 us), else 64-token ones (M = 128 there: 36 against 38 us).
+    // 256 x 256 tiles (eight waves, half the copy bytes per flop) when they
+    // fill whole rounds of one workgroup per CU, or one round nearly (192 to
+    // 256 of them); 128-token tiles once those still give two workgroups per
+    // CU (at T = 8, H = 4096, M = 256 / 512 / 768: 68 / 100 / 138 -> 47 /
+    // 90 / 120 us); else 64-token ones (M = 128 there: 36 against 38 us).
+    // 256 x 256 against 128-channel tiles, same bits (us, operands resident
+    // in the last-level cache): T = 8, Kr = 1376, H = 4096, M = 512 / 1024
+    // (256 / 512 tiles): 73.9 / 141.8 -> 68.7 / 128.6; T = 8, Kr = 704,
+    // H = 2048, M = 1024 / 1920: 52.5 / 100.2 -> 49.7 / 96.2; T = 8,
+    // Kr = 512, M = 512: 46.6 -> 43.1; T = 16, Kr = 688, M = 256 / 512:
+    // 61.2 / 115.8 -> 57.8 / 109.0; 192 and 216 tiles (T = 4, M = 768;
+    // T = 8, Kr = 384, H = 768, M = 2304): 60.3 / 39.9 -> 53.5 / 36.4.
+    // Slower at 384 tiles (1.5 rounds: +4 to +10%) and below 192 (+25 to
+    // +60%), and at T = 4, Kr = 1376, M = 960 (256 tiles): 64.4 -> 66.9.
     const int tm = (H + kSplitBM - 1) / kSplitBM;
     const long long wg128 = (long long)T * tm * ((M + 127) / 128);
-    if (wg128 >= 512) {
+    const int tm2 = (H + 255) / 256, tn2 = (M + 255) / 256;
+    const long long wg256 = (long long)T * tm2 * tn2;
+    if (wg256 % kCUs == 0 || (wg256 >= 192 && wg256 < kCUs)) {
+      hipLaunchKernelGGL((rowpar_pcr_split_kernel<256, 256, kBigTileWaves>), dim3((unsigned)wg256),
+                         dim3(kBigTileWaves * 64), 0, s, X, W, out, Y, M, Kr, H, tm2, tn2);
+    } else if (wg128 >= 512) {
       const int tn = (M + 127) / 128;
       hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 128, kSplitNW>), dim3(T * tm * tn), dim3(kSplitNW * 64), 0,
                          s, X, W, out, Y, M, Kr, H, tm, tn);

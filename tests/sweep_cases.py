@@ -13,6 +13,9 @@ def forward_path(T, M, Kr, H):
     walk = T * nk
     limit = 128 if nk <= 2 else (3 * walk + 128 if T <= 8 else 2 * walk + 64)
     if T >= 2 and tiles64 <= limit:
+        wg256 = T * -(-H // 256) * -(-M // 256)
+        if wg256 % 256 == 0 or 192 <= wg256 < 256:
+            return "split256"
         return "split128" if T * -(-H // 128) * -(-M // 128) >= 512 else "split64"
     if M <= 192 and H <= 65536:
         return "chunked"
@@ -44,5 +47,9 @@ def cases(n=64, seed=2026):
             (8, 3000, 96, 512, "random", 0.5, 15), (5, 2500, 200, 264, "random", 0.5, 16),
             # the largest rank count the library takes
             (64, 20, 16, 264, "random", 0.5, 17), (64, 100, 72, 128, "strided", 0.5, 18),
-            (64, 900, 8, 64, "random", 0.5, 19), (64, 8256, 8, 64, "prefix", 0.5, 20)]
+            (64, 900, 8, 64, "random", 0.5, 19), (64, 8256, 8, 64, "prefix", 0.5, 20),
+            # split forward with 256x256 tiles: 192 of them (ragged tokens), 256
+            # (ragged channels), 256 at T = 16
+            (8, 1800, 136, 768, "random", 0.5, 21), (8, 1900, 200, 776, "strided", 0.5, 22),
+            (16, 2000, 72, 512, "random", 0.5, 23)]
     return out

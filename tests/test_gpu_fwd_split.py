@@ -1,10 +1,12 @@
 """The forward for token counts between decode and full tiles: one workgroup
-per (rank, 128-channel block, 64-token block), the cross-rank sum done by the
-last workgroup of each block to finish.  Integer inputs bit for bit against
-the oracle (blocks with and without synced channels, ragged token, channel
-and contraction counts, up to 13 ranks, the column-parallel layer with no
-mask), Gaussian inputs at the Llama2-7B down-projection with 512 tokens, one
-workspace shared by calls of every path, and run-to-run bits."""
+per (rank, channel block, token block) -- tiles of 128 x 64, 128 x 128 or
+256 x 256 -- writing that rank's fp32 product tile, then a streaming pass that
+forms the partial channel-reduce.  Integer inputs bit for bit against the
+oracle (blocks with and without synced channels, ragged token, channel and
+contraction counts, up to 13 ranks, all three tile sizes, the column-parallel
+layer with no mask), Gaussian inputs at the Llama2-7B down-projection with 512
+tokens (256 x 256 tiles), one workspace shared by calls of every path, and
+run-to-run bits."""
 import numpy as np
 import pytest
 import torch
@@ -36,10 +38,13 @@ def _mask(H, kind, p, seed):
     return synth.make_mask(H, p, kind, seed=seed)
 
 
-# (T, M, Kr, H): M from 33 (one partial token block) to 1000; H = 776 leaves
-# a partial channel block (6 x 128 + 8)
+# (T, M, Kr, H): M from 33 (one partial token block) to 1900; H = 776 leaves
+# a partial channel block (6 x 128 + 8, 3 x 256 + 8).  The first six run
+# 128 x 64 tiles; (8, 1000, 136, 1032) 576 tiles of 128 x 128 (1032 = 8 x 128
+# + 8); the last two 256 x 256 tiles: 192 of them with a partial token block
+# (1800 = 7 x 256 + 8), and 256 with partial channel and token blocks.
 SHAPES = [(2, 33, 40, 776), (3, 100, 136, 776), (8, 257, 96, 1024), (8, 1000, 64, 776), (13, 64, 72, 520),
-          (4, 130, 1376, 512)]
+          (4, 130, 1376, 512), (8, 1000, 136, 1032), (8, 1800, 136, 768), (8, 1900, 200, 776)]
 MASKS = [("random", 0.5), ("prefix", 0.5), ("strided", 0.5), ("random", 0.0), ("random", 1.0), ("blocks", 0.0)]
 
 
