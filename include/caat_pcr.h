@@ -84,7 +84,10 @@ const char* caat_status_string(int status);
  *     CUs) writes fp32
  *     products Y[T,M,H] into the workspace, and a streaming pass reduces
  *     them into out (the synced sum is the ascending-rank fp32 sum of the
- *     per-rank products);
+ *     per-rank products).  With at most 256 tiles of 128 x 64 and at least
+ *     16 chunks of 64 per rank's contraction, each rank's contraction is
+ *     cut in two slices whose fp32 products (twice the workspace) are added
+ *     first;
  *   - otherwise the fused tile kernel (each tile walks all T ranks), which
  *     needs no workspace.
  * caat_rowpar_pcr_fwd_workspace_bytes() gives the bytes a call needs (0:
@@ -108,9 +111,10 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  * Calls that need a workspace use a scratch area owned by the library
  * instead, a static device array of CAAT_NOALLOC_SCRATCH_BYTES (16 MiB) on
  * each GPU, held until the process ends.  A split-path call whose fp32
- * products would exceed it runs the path the shape would take without the
- * split (chunked decode or fused tiles: the same value up to fp32 summation
- * order); a decode call whose partials exceed it (e.g. T*H > 131056 channels
+ * products would exceed it cuts the contraction into fewer slices, or, if
+ * even whole contractions do not fit, runs the path the shape would take
+ * without the split (chunked decode or fused tiles); either gives the same
+ * value up to fp32 summation order.  A decode call whose partials exceed it (e.g. T*H > 131056 channels
  * over all ranks at M = 32) returns CAAT_ERR_WORKSPACE before anything is
  * enqueued.  The scratch of the device current at the call is
  * used (`stream` must belong to it); its arrival counters are cleared by the

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "decode_kernel.hpp"
@@ -190,17 +191,19 @@ static uint32_t reduce_groups(const dim3& grid, long long slice_bytes, int T) {
 
 // Partial channel-reduce of fp32 y[T,M,H] into bf16 o (the split forward's
 // second pass).
-int launch_reduce_f32_bf16(const float* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, hipStream_t s) {
-  const long long mh = (long long)M * H;
+// (ks contraction slices per rank: y[q][t] at y + (q * T + t) * M * H.)
+int launch_reduce_f32_bf16(const float* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, int ks,
+                           hipStream_t s) {
+  const long long mh = (long long)M * H, ss = (long long)T * mh;
   const uint32_t nvec = (uint32_t)(mh / 4);
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
   const uint32_t hv = (uint32_t)(H / 4);
   const uint32_t hf = reduce_groups(grid, mh * 4, T);
   switch (T) {
-    case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
-    case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
-    case 8: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
-    default: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf); break;
+    case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
+    case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
+    case 8: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
+    default: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
   }
   return launched();
 }
@@ -291,18 +294,53 @@ static bool use_split(int T, int M, int Kr, int H) {
   return T >= 2 && M >= kSplitMinM && tiles <= limit;
 }
 
-// Workspace of a forward with a mask; `split` = whether the split path may
-// be taken (the allocation-free entry point declines it when its fp32 tiles
-// would not fit the library's scratch array).
-static size_t fwd_need(int T, int M, int Kr, int H, bool split) {
-  if (split && use_split(T, M, Kr, H)) return kDecCounterBytes + round256((size_t)T * M * H * sizeof(float));
+// Slices of each rank's contraction in the split forward's 128 x 64 tiles:
+// two when those tiles leave at most one workgroup per CU and each rank's
+// contraction is long (at least 16 chunks), so that every CU runs two
+// workgroups of half the walk; the fp32 products then take twice the
+// workspace.  Measured on MI355X (random S, us, 1 -> 2 slices, operands
+// resident in the last-level cache): T = 8, Kr = 1376, H = 4096, M = 33 /
+// 64: 22.9 / 27.7 -> 22.0 / 24.6; T = 4, M = 64 / 128: 20.8 / 22.0 ->
+// 17.9 / 19.1; T = 2, M = 64 / 256: 14.4 / 20.5 -> 12.7 / 20.1.  Slower
+// with 512 workgroups (T = 8, M = 96: 24.9 -> 30.9) and with short
+// contractions (Kr = 512 or 704, 8 or 11 chunks: +10 to +15%); four slices
+// were slower than two everywhere but at T = 4, M = 64 (17.0 us).
+constexpr int kMaxSplitKs = 2;
+static int split_ks_rule(int T, int M, int Kr, int H) {
+  const long long wg = (long long)T * ((H + 127) / 128) * ((M + 63) / 64);
+  const int nk = (Kr + kBK - 1) / kBK;
+  return wg <= kCUs && nk >= 16 ? 2 : 1;
+}
+
+// Tiles of the split forward, and the number of slices each rank's
+// contraction is cut into.
+struct SplitPlan {
+  int bm, bn, ks;
+};
+static SplitPlan split_plan(int T, int M, int Kr, int H) {
+  const long long wg128 = (long long)T * ((H + 127) / 128) * ((M + 127) / 128);
+  const long long wg256 = (long long)T * ((H + 255) / 256) * ((M + 255) / 256);
+  if (wg256 % kCUs == 0 || (wg256 >= 192 && wg256 < kCUs)) return {256, 256, 1};
+  if (wg128 >= 512) return {128, 128, 1};
+  return {128, 64, split_ks_rule(T, M, Kr, H)};
+}
+
+// Workspace of a forward with a mask; `split` = the most contraction slices
+// the split path may use, 0 = not at all (the allocation-free entry point
+// lowers it, or declines the split, when the fp32 products would not fit the
+// library's scratch array).
+static size_t fwd_need(int T, int M, int Kr, int H, int split) {
+  if (split > 0 && use_split(T, M, Kr, H)) {
+    const int ks = std::min(split, split_plan(T, M, Kr, H).ks);
+    return kDecCounterBytes + round256((size_t)ks * T * M * H * sizeof(float));
+  }
   if (!use_decode(M, H)) return 0;
   return decode_counter_bytes(H) + round256((size_t)T * (M < kDecMaxM ? M : kDecMaxM) * H * sizeof(float));
 }
 
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
   if (check_dims(T, M, Kr, H) != CAAT_OK) return 0;
-  return fwd_need(T, M, Kr, H, true);
+  return fwd_need(T, M, Kr, H, kMaxSplitKs);
 }
 
 }  // extern "C"
@@ -326,10 +364,10 @@ int fwd_check_args(const uint16_t* X, const uint16_t* W, const uint8_t* mask, co
 // kernel's arrival counters (kDecCounterBytes, zero on entry) and then its
 // fp32 partials; it is only touched for decode-shaped calls with a mask.
 int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
-               int H, void* workspace, hipStream_t s, bool split = true) {
+               int H, void* workspace, hipStream_t s, int split = kMaxSplitKs) {
   if (M == 0) return CAAT_OK;
   if (!mask) workspace = nullptr;  // never touched without synced channels
-  if (split && use_split(T, M, Kr, H)) {
+  if (split > 0 && use_split(T, M, Kr, H)) {
     float* Y = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kDecCounterBytes) : nullptr;
     // 256 x 256 tiles (eight waves, half the copy bytes per flop) when they
     // fill whole rounds of one workgroup per CU, or one round nearly (192 to
@@ -345,24 +383,21 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
     // T = 8, Kr = 384, H = 768, M = 2304): 60.3 / 39.9 -> 53.5 / 36.4.
     // Slower at 384 tiles (1.5 rounds: +4 to +10%) and below 192 (+25 to
     // +60%), and at T = 4, Kr = 1376, M = 960 (256 tiles): 64.4 -> 66.9.
-    const int tm = (H + kSplitBM - 1) / kSplitBM;
-    const long long wg128 = (long long)T * tm * ((M + 127) / 128);
-    const int tm2 = (H + 255) / 256, tn2 = (M + 255) / 256;
-    const long long wg256 = (long long)T * tm2 * tn2;
-    if (wg256 % kCUs == 0 || (wg256 >= 192 && wg256 < kCUs)) {
-      hipLaunchKernelGGL((rowpar_pcr_split_kernel<256, 256, kBigTileWaves>), dim3((unsigned)wg256),
-                         dim3(kBigTileWaves * 64), 0, s, X, W, out, Y, M, Kr, H, tm2, tn2);
-    } else if (wg128 >= 512) {
-      const int tn = (M + 127) / 128;
-      hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 128, kSplitNW>), dim3(T * tm * tn), dim3(kSplitNW * 64), 0,
-                         s, X, W, out, Y, M, Kr, H, tm, tn);
-    } else {
-      const int tn = (M + 63) / 64;
-      hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 64, kSplitNW>), dim3(T * tm * tn), dim3(kSplitNW * 64), 0,
-                         s, X, W, out, Y, M, Kr, H, tm, tn);
-    }
+    const SplitPlan pl = split_plan(T, M, Kr, H);
+    const int ks = Y ? std::min(split, pl.ks) : 1;  // bf16 straight to out: whole contractions
+    const int tm = (H + pl.bm - 1) / pl.bm, tn = (M + pl.bn - 1) / pl.bn;
+    const dim3 grid((unsigned)((long long)T * ks * tm * tn));
+    if (pl.bm == 256)
+      hipLaunchKernelGGL((rowpar_pcr_split_kernel<256, 256, kBigTileWaves>), grid, dim3(kBigTileWaves * 64), 0, s, X,
+                         W, out, Y, T, M, Kr, H, tm, tn, ks);
+    else if (pl.bn == 128)
+      hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 128, kSplitNW>), grid, dim3(kSplitNW * 64), 0, s, X, W,
+                         out, Y, T, M, Kr, H, tm, tn, ks);
+    else
+      hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 64, kSplitNW>), grid, dim3(kSplitNW * 64), 0, s, X, W,
+                         out, Y, T, M, Kr, H, tm, tn, ks);
     if (int st = launched()) return st;
-    return Y ? launch_reduce_f32_bf16(Y, mask, out, T, M, H, s) : CAAT_OK;
+    return Y ? launch_reduce_f32_bf16(Y, mask, out, T, M, H, ks, s) : CAAT_OK;
   }
   if (use_decode(M, H)) {
     // workspace: the per-block arrival counters, then the fp32 partials
@@ -472,9 +507,11 @@ int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint
                                 int M, int Kr, int H, void* stream) {
   if (!mask) return CAAT_ERR_NULL;
   if (int st = fwd_check_args(X, W, mask, out, T, M, Kr, H)) return st;
-  // The split path's fp32 tiles may not fit the scratch array; such calls
-  // take the tiled or chunked decode path instead (no scratch, or a chunk's).
-  const bool split = fwd_need(T, M, Kr, H, true) <= kScratchBytes;
+  // The split path's fp32 products may not fit the scratch array: then
+  // fewer contraction slices, or, if even one does not fit, the tiled or
+  // chunked decode path (no scratch, or a chunk's).
+  int split = kMaxSplitKs;
+  while (split > 0 && fwd_need(T, M, Kr, H, split) > kScratchBytes) split /= 2;
   const size_t need = fwd_need(T, M, Kr, H, split);
   if (need > kScratchBytes) return CAAT_ERR_WORKSPACE;
   if (M == 0) return CAAT_OK;

@@ -101,11 +101,14 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
 // out[t] = bf16 of the partial channel-reduce of the fp32 per-rank products
 // Y[T,M,H]: on synced channels the ascending-rank fp32 sum starting from rank
 // 0's value, elsewhere Y[t]; one thread per 4-channel vector, T 16-byte loads
-// and T 8-byte stores.
+// and T 8-byte stores.  With ks > 1 the products come in ks contraction
+// slices, Y[q][t] at Y + q * sstride + t * mh, and rank t's value is their
+// fp32 sum in slice order.
 template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
-                           int T_rt, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups) {
+                           int T_rt, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups, int ks,
+                           long long sstride) {
   const int T = TC > 0 ? TC : T_rt;
   constexpr int NR = TC > 0 ? TC : 1;  // ranks kept in registers
   const uint32_t v = reduce_block(groups) * kReduceThreads + threadIdx.x;
@@ -115,21 +118,33 @@ pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restric
   const uint32_t mk = *reinterpret_cast<const uint32_t*>(mask + c);
   const bool s0 = (mk & 0xffu) != 0, s1 = (mk & 0xff00u) != 0;
   const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
+  // Runtime T: a rank's product (its slices in slice order) is read twice,
+  // for the sum and for the output, with plain loads so the second read
+  // finds the lines in cache.
+  auto rank_value = [&](int t) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+    for (int q = 1; q < ks; ++q) a += *reinterpret_cast<const f32x4*>(Y + q * sstride + t * mh + base);
+    return a;
+  };
   f32x4 y[NR];
   f32x4 s;
   if (TC > 0) {
 #pragma unroll
     for (int t = 0; t < NR; ++t) y[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + t * mh + base));
+    for (int q = 1; q < ks; ++q)
+#pragma unroll
+      for (int t = 0; t < NR; ++t)
+        y[t] += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + q * sstride + t * mh + base));
     s = y[0];
 #pragma unroll
     for (int t = 1; t < NR; ++t) s += y[t];
   } else {
-    s = *reinterpret_cast<const f32x4*>(Y + base);
-    for (int t = 1; t < T; ++t) s += *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+    s = rank_value(0);
+    for (int t = 1; t < T; ++t) s += rank_value(t);
   }
 #pragma unroll 8
   for (int t = 0; t < T; ++t) {
-    const f32x4 yt = TC > 0 ? y[t < NR ? t : 0] : *reinterpret_cast<const f32x4*>(Y + t * mh + base);
+    const f32x4 yt = TC > 0 ? y[t < NR ? t : 0] : rank_value(t);
     u32x2 o;
     o[0] = pack_bf16x2(s0 ? s.x : yt.x, s1 ? s.y : yt.y);
     o[1] = pack_bf16x2(s2 ? s.z : yt.z, s3 ? s.w : yt.w);

@@ -30,10 +30,13 @@ namespace caat {
 constexpr int kSplitBM = 128;
 constexpr int kSplitNW = 4;
 
+// With ks > 1 (fp32 products only) each rank's contraction is cut into ks
+// slices of whole chunks, one workgroup each, and slice q of rank t goes to
+// Y[q][t]; the second pass adds a rank's slices in slice order first.
 template <int BM, int BN, int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
 rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
-                        float* __restrict__ Y, int M, int Kr, int H, int tiles_m, int tiles_n) {
+                        float* __restrict__ Y, int T, int M, int Kr, int H, int tiles_m, int tiles_n, int ks) {
   using S = TileShape<BM, BN, NW>;
   using RS = RowStage<S::WM>;
   static_assert(NW * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
@@ -43,8 +46,9 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int per_rank = tiles_m * tiles_n;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = lin / per_rank;
-  const int tile = lin - t * per_rank;
+  const int tq = lin / per_rank;  // t * ks + q
+  const int t = tq / ks, q = tq - t * ks;
+  const int tile = lin - tq * per_rank;
   int tm, tn;
   tile_coords(tile, tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, m0 = tn * BN;  // channel block, token block
@@ -52,6 +56,8 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
   const int tkw = m0 + wn * S::WN;       // this wave's first token
   const int nk = (Kr + kBK - 1) / kBK;
   const int kv_last = Kr - (nk - 1) * kBK;
+  const int kcs = (nk + ks - 1) / ks;              // chunks per slice
+  const int cb = q * kcs, ce = min(nk, cb + kcs);  // this slice: chunks cb .. ce-1 (none past nk)
   const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
 
   f32x16 acc[S::WI][S::WJ];
@@ -63,8 +69,8 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     da.template load<NW>(H, c0, c * kBK, buf, wave);
     db.load<BN, NW>(Kr, m0, c * kBK, buf + BM * kBK, wave);
   };
-  issue(0);
-  for (int c = 0; c < nk; ++c) {
+  if (cb < ce) issue(cb);
+  for (int c = cb; c < ce; ++c) {
     uint16_t* As = smem + (c & 1) * S::BUF;
     uint16_t* Bs = As + BM * kBK;
     __builtin_amdgcn_s_waitcnt(0);
@@ -76,7 +82,7 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     mma_chunk<BM, BN, NW>([&](int ks, int i) { return frag_mncont<BM>(As, wm * S::WM + i * 32, ks, lane); },
                           [&](int ks, int j) { return frag_kcont(Bs, wn * S::WN + j * 32, ks, lane); }, acc,
                           [&] {
-                            if (c + 1 < nk) issue(c + 1);
+                            if (c + 1 < ce) issue(c + 1);
                           });
   }
 
@@ -97,18 +103,18 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     });
     return;
   }
-  // fp32 to Y[t]: accumulator registers 4q..4q+3 of block (i, j) are 4
+  // fp32 to Y[q][t]: accumulator registers 4r..4r+3 of block (i, j) are 4
   // consecutive channels of one token.
-  float* yt = Y + t * MH;
+  float* yt = Y + ((long long)q * T + t) * MH;
 #pragma unroll
   for (int i = 0; i < S::WI; ++i)
 #pragma unroll
     for (int j = 0; j < S::WJ; ++j) {
       const int tok = tkw + j * 32 + (lane & 31);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = chw + i * 32 + q * 8 + (lane >> 5) * 4;
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      for (int r = 0; r < 4; ++r) {
+        const int ch = chw + i * 32 + r * 8 + (lane >> 5) * 4;
+        const f32x4 v = {acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]};
         if (tok < M && ch < H) *reinterpret_cast<f32x4*>(yt + (long long)tok * H + ch) = v;
       }
     }

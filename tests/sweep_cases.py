@@ -16,7 +16,10 @@ def forward_path(T, M, Kr, H):
         wg256 = T * -(-H // 256) * -(-M // 256)
         if wg256 % 256 == 0 or 192 <= wg256 < 256:
             return "split256"
-        return "split128" if T * -(-H // 128) * -(-M // 128) >= 512 else "split64"
+        if T * -(-H // 128) * -(-M // 128) >= 512:
+            return "split128"
+        # two contraction slices per rank: few 128x64 tiles, long contractions
+        return "split64x2" if tiles64 * T <= 256 and nk >= 16 else "split64"
     if M <= 192 and H <= 65536:
         return "chunked"
     if -(-M // 256) * -(-H // 256) >= 256:
@@ -51,5 +54,7 @@ def cases(n=64, seed=2026):
             # split forward with 256x256 tiles: 192 of them (ragged tokens), 256
             # (ragged channels), 256 at T = 16
             (8, 1800, 136, 768, "random", 0.5, 21), (8, 1900, 200, 776, "strided", 0.5, 22),
-            (16, 2000, 72, 512, "random", 0.5, 23)]
+            (16, 2000, 72, 512, "random", 0.5, 23),
+            # split forward, two contraction slices per rank (17 chunks: 9 + 8)
+            (4, 100, 1048, 512, "random", 0.5, 24)]
     return out

@@ -121,9 +121,17 @@ def test_workspace_sizes(L):
     T, Kr, H = 8, 1376, 4096
     # 33 .. 1280 tokens at this width (at most 3 x 176 + 128 = 656 fused
     # tiles of 128 x 64 for a walk of 8 x 22 chunks): the split forward's
-    # fp32 products after the counter region
-    for M in (33, 100, 193, 1280):
+    # fp32 products after the counter region -- two contraction slices of
+    # them while there are at most 256 tiles of 128 x 64 (M <= 64 here)
+    for M in (33, 64):
+        assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == 2048 + 2 * T * M * H * 4
+    for M in (65, 100, 193, 1280):
         assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, M, Kr, H) == 2048 + T * M * H * 4
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(4, 128, Kr, H) == 2048 + 2 * 4 * 128 * H * 4  # 256 tiles
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(4, 129, Kr, H) == 2048 + 4 * 129 * H * 4  # 384 tiles
+    # slices only for contractions of at least 16 chunks of 64
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 64, 960, H) == 2048 + T * 64 * H * 4  # 15 chunks
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 64, 968, H) == 2048 + 2 * T * 64 * H * 4  # 16 chunks
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 1281, Kr, H) == 0  # 672 tiles: fused, no workspace
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 640, 512, H) == 2048 + T * 640 * H * 4  # 320 tiles, walk 64
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 641, 512, H) == 0  # 352 tiles: fused

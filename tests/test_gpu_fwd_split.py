@@ -1,7 +1,8 @@
 """The forward for token counts between decode and full tiles: one workgroup
 per (rank, channel block, token block) -- tiles of 128 x 64, 128 x 128 or
-256 x 256 -- writing that rank's fp32 product tile, then a streaming pass that
-forms the partial channel-reduce.  Integer inputs bit for bit against the
+256 x 256, and with few tiles and long contractions one per slice of the
+contraction -- writing that rank's fp32 product tile, then a streaming pass
+that forms the partial channel-reduce.  Integer inputs bit for bit against the
 oracle (blocks with and without synced channels, ragged token, channel and
 contraction counts, up to 13 ranks, all three tile sizes, the column-parallel
 layer with no mask), Gaussian inputs at the Llama2-7B down-projection with 512
@@ -39,12 +40,15 @@ def _mask(H, kind, p, seed):
 
 
 # (T, M, Kr, H): M from 33 (one partial token block) to 1900; H = 776 leaves
-# a partial channel block (6 x 128 + 8, 3 x 256 + 8).  The first six run
-# 128 x 64 tiles; (8, 1000, 136, 1032) 576 tiles of 128 x 128 (1032 = 8 x 128
+# a partial channel block (6 x 128 + 8, 3 x 256 + 8).  The first seven run
+# 128 x 64 tiles, (4, 130, 1376, 512) and (3, 40, 1048, 264) with each rank's
+# contraction in two slices (22 chunks, the last a half one: 11 + 11; 17
+# chunks: 9 + 8); (8, 1000, 136, 1032) 576 tiles of 128 x 128 (1032 = 8 x 128
 # + 8); the last two 256 x 256 tiles: 192 of them with a partial token block
 # (1800 = 7 x 256 + 8), and 256 with partial channel and token blocks.
 SHAPES = [(2, 33, 40, 776), (3, 100, 136, 776), (8, 257, 96, 1024), (8, 1000, 64, 776), (13, 64, 72, 520),
-          (4, 130, 1376, 512), (8, 1000, 136, 1032), (8, 1800, 136, 768), (8, 1900, 200, 776)]
+          (4, 130, 1376, 512), (3, 40, 1048, 264), (8, 1000, 136, 1032), (8, 1800, 136, 768),
+          (8, 1900, 200, 776)]
 MASKS = [("random", 0.5), ("prefix", 0.5), ("strided", 0.5), ("random", 0.0), ("random", 1.0), ("blocks", 0.0)]
 
 
@@ -151,3 +155,39 @@ def test_noalloc_split_fallback(ops):
     G.check_bf16(got, oracle.rowpar_pcr_fwd(X, W, mask), (mask != 0)[None, None, :], "noalloc split fallback")
     s = np.flatnonzero(mask)
     assert all(np.array_equal(got[0][:, s], got[t][:, s]) for t in range(1, T))
+
+
+def test_noalloc_fewer_slices(ops):
+    """The Llama2-7B down-projection at 64 tokens cuts each rank's contraction
+    in two slices (2 x 8.4 MB of fp32 products, over the 16 MiB scratch); the
+    allocation-free forward then runs whole contractions (8.4 MB).  Integer
+    inputs bit for bit against the oracle on both entry points; Gaussian ones
+    within the bar on both, and the two agree to the bf16 rounding of
+    different fp32 summation orders."""
+    T, M, Kr, H = 8, 64, 1376, 4096
+    assert ops.fwd_workspace_bytes(T, M, Kr, H) == 2048 + 2 * T * M * H * 4 > (16 << 20)
+    _announce(f"noalloc fewer slices T={T} M={M} Kr={Kr} H={H}")
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=34, lo=-1, hi=1, x_zero_frac=0.97)
+    mask = synth.make_mask(H, 0.5, "random", seed=34)
+    ref = oracle.rowpar_pcr_fwd(X, W, mask)
+    assert np.abs(ref).max() <= 256
+    args = (G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
+    out_n = torch.full((T, M, H), 7.0, dtype=torch.bfloat16, device=G.dev())
+    ops.rowpar_pcr_fwd_noalloc(*args, out_n)
+    out_w = ops.rowpar_pcr_fwd(*args)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(out_n), ref)
+    assert np.array_equal(G.from_dev_bf16(out_w), ref)
+    X, W = synth.make_fwd_inputs(T, M, Kr, H, seed=35)
+    args = (G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
+    ops.rowpar_pcr_fwd_noalloc(*args, out_n)
+    out_w = ops.rowpar_pcr_fwd(*args)
+    torch.cuda.synchronize()
+    ref = oracle.rowpar_pcr_fwd(X, W, mask)
+    cls = (mask != 0)[None, None, :]
+    got_n, got_w = G.from_dev_bf16(out_n), G.from_dev_bf16(out_w)
+    G.check_bf16(got_n, ref, cls, "noalloc, whole contractions")
+    G.check_bf16(got_w, ref, cls, "two contraction slices")
+    s = np.flatnonzero(mask)
+    for got in (got_n, got_w):
+        assert all(np.array_equal(got[0][:, s], got[t][:, s]) for t in range(1, T))
