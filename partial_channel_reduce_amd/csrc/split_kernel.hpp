@@ -4,9 +4,11 @@
 // The fused forward gives each (channel tile, token tile) to one workgroup,
 // which walks all T ranks' contractions in turn.  With a few hundred tokens
 // that leaves too few tiles to fill the chip, each with a long serial walk.
-// Here every (rank t, 128-channel block, 64- or 128-token block) is a workgroup of its
-// own and computes only Y_t's tile (the same copy and MFMA loop as the fused
-// forward, over rank t's contraction):
+// Here every (rank t, channel block, token block) is a workgroup of its own
+// (tiles of 128 x 64, 128 x 128 or 256 x 256; with few tiles and a long
+// contraction, one workgroup per slice of it) and computes only Y_t's tile
+// (the same copy and MFMA loop as the fused forward, over rank t's
+// contraction):
 //   * with no mask (the column-parallel layer: nothing synced) it writes the
 //     tile to out[t] in bf16;
 //   * otherwise it writes the fp32 tile to Y[t] in the workspace, and a
