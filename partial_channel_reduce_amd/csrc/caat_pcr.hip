@@ -266,10 +266,11 @@ static_assert(kDecCounterBytes % 256 == 0, "partials stay 256-byte aligned");
 static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 
 // Token counts between decode and full tiles: the rank walk split across
-// workgroups, one per (rank, 128-channel block, 64-token block), each
-// writing its rank's fp32 product tile into the workspace (after the decode
-// kernel's counter region, which this path leaves alone), then one
-// streaming pass forms the partial channel-reduce into out.
+// workgroups, one per (rank, channel block, token block) with the tiles and
+// contraction slices of split_plan below, each writing its rank's fp32
+// product tile into the workspace (after the decode kernel's counter region,
+// which this path leaves alone), then one streaming pass forms the partial
+// channel-reduce into out.
 // It pays while the fused kernel is short of tiles (of 128 channels x 64
 // tokens) for the length of its serial walk, walk = T x ceil(Kr/64) chunks:
 // up to 3 x walk + 128 tiles with T <= 8, 2 x walk + 64 with more ranks (the
@@ -313,7 +314,20 @@ static int split_ks_rule(int T, int M, int Kr, int H) {
 }
 
 // Tiles of the split forward, and the number of slices each rank's
-// contraction is cut into.
+// contraction is cut into.  256 x 256 tiles (eight waves, half the copy
+// bytes per flop) when they fill whole rounds of one workgroup per CU, or one
+// round nearly (192 to 256 of them); 128-token tiles once those still give
+// two workgroups per CU (at T = 8, H = 4096, M = 256 / 512 / 768: 68 / 100 /
+// 138 -> 47 / 90 / 120 us); else 64-token ones (M = 128 there: 36 against
+// 38 us).  256 x 256 against 128-channel tiles, same bits (us, operands
+// resident in the last-level cache): T = 8, Kr = 1376, H = 4096, M = 512 /
+// 1024 (256 / 512 tiles): 73.9 / 141.8 -> 68.7 / 128.6; T = 8, Kr = 704,
+// H = 2048, M = 1024 / 1920: 52.5 / 100.2 -> 49.7 / 96.2; T = 8, Kr = 512,
+// M = 512: 46.6 -> 43.1; T = 16, Kr = 688, M = 256 / 512: 61.2 / 115.8 ->
+// 57.8 / 109.0; 192 and 216 tiles (T = 4, M = 768; T = 8, Kr = 384, H = 768,
+// M = 2304): 60.3 / 39.9 -> 53.5 / 36.4.  Slower at 384 tiles (1.5 rounds:
+// +4 to +10%) and below 192 (+25 to +60%), and at T = 4, Kr = 1376, M = 960
+// (256 tiles): 64.4 -> 66.9.
 struct SplitPlan {
   int bm, bn, ks;
 };
@@ -360,29 +374,17 @@ int fwd_check_args(const uint16_t* X, const uint16_t* W, const uint8_t* mask, co
   return CAAT_OK;
 }
 
-// Kernel launches of a validated forward.  `workspace` holds the decode
-// kernel's arrival counters (kDecCounterBytes, zero on entry) and then its
-// fp32 partials; it is only touched for decode-shaped calls with a mask.
+// Kernel launches of a validated forward.  `workspace` starts with the
+// decode kernel's arrival counters (kDecCounterBytes, zero on entry); after
+// them come the decode kernel's fp32 partials or the split path's fp32
+// products (at most `split` contraction slices of them; 0 = no split path).
+// Only calls with a mask on those two paths touch it.
 int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
                int H, void* workspace, hipStream_t s, int split = kMaxSplitKs) {
   if (M == 0) return CAAT_OK;
   if (!mask) workspace = nullptr;  // never touched without synced channels
   if (split > 0 && use_split(T, M, Kr, H)) {
     float* Y = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kDecCounterBytes) : nullptr;
-    // 256 x 256 tiles (eight waves, half the copy bytes per flop) when they
-    // fill whole rounds of one workgroup per CU, or one round nearly (192 to
-    // 256 of them); 128-token tiles once those still give two workgroups per
-    // CU (at T = 8, H = 4096, M = 256 / 512 / 768: 68 / 100 / 138 -> 47 /
-    // 90 / 120 us); else 64-token ones (M = 128 there: 36 against 38 us).
-    // 256 x 256 against 128-channel tiles, same bits (us, operands resident
-    // in the last-level cache): T = 8, Kr = 1376, H = 4096, M = 512 / 1024
-    // (256 / 512 tiles): 73.9 / 141.8 -> 68.7 / 128.6; T = 8, Kr = 704,
-    // H = 2048, M = 1024 / 1920: 52.5 / 100.2 -> 49.7 / 96.2; T = 8,
-    // Kr = 512, M = 512: 46.6 -> 43.1; T = 16, Kr = 688, M = 256 / 512:
-    // 61.2 / 115.8 -> 57.8 / 109.0; 192 and 216 tiles (T = 4, M = 768;
-    // T = 8, Kr = 384, H = 768, M = 2304): 60.3 / 39.9 -> 53.5 / 36.4.
-    // Slower at 384 tiles (1.5 rounds: +4 to +10%) and below 192 (+25 to
-    // +60%), and at T = 4, Kr = 1376, M = 960 (256 tiles): 64.4 -> 66.9.
     const SplitPlan pl = split_plan(T, M, Kr, H);
     const int ks = Y ? std::min(split, pl.ks) : 1;  // bf16 straight to out: whole contractions
     const int tm = (H + pl.bm - 1) / pl.bm, tn = (M + pl.bn - 1) / pl.bn;
@@ -474,7 +476,7 @@ namespace {
 
 // ---- forward without a caller workspace -----------------------------------
 // Library-owned scratch for the decode kernel's arrival counters and fp32
-// partials, one copy per GPU (each device holds its own instance of this
+// partials, or the split path's fp32 products, one copy per GPU (each device holds its own instance of this
 // array, at its own address, until the process ends; it starts zeroed).  In
 // host code the array's name is only a host-side stand-in: kernels get the
 // device address that hipGetSymbolAddress returns for the current device.
