@@ -151,8 +151,9 @@ def rowpar_pcr_fwd(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: to
 
 def rowpar_pcr_fwd_noalloc(X: torch.Tensor, W: torch.Tensor, mask: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
     """rowpar_pcr_fwd into a caller-provided `out`, with no workspace: the
-    library's per-GPU scratch serves decode-shaped calls (see caat_pcr.h).
-    Calls that may overlap on one GPU must be serialised by the caller."""
+    library's per-GPU scratch serves the decode and split paths where their
+    workspace fits it (see caat_pcr.h).  Calls that may overlap on one GPU
+    must be serialised by the caller."""
     _require(X, "X", torch.bfloat16, 3)
     dev = X.device
     _require(W, "W", torch.bfloat16, 3, dev)
