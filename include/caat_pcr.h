@@ -79,15 +79,14 @@ const char* caat_status_string(int status);
  *   - 33 <= M, T >= 2, while the fused kernel below would have few tiles for
  *     its walk over the ranks (ceil(H/128) * ceil(M/64) at most
  *     3 * T * ceil(Kr/64) + 128 with T <= 8, 2 * T * ceil(Kr/64) + 64 with
- *     more, 128 when Kr <= 128): one workgroup per (rank, 128 channels x 64
- *     or 128 tokens, or 256 x 256 when those fill whole rounds of the 256
- *     CUs) writes fp32
- *     products Y[T,M,H] into the workspace, and a streaming pass reduces
- *     them into out (the synced sum is the ascending-rank fp32 sum of the
- *     per-rank products).  With at most 256 tiles of 128 x 64 and at least
- *     16 chunks of 64 per rank's contraction, each rank's contraction is
- *     cut in two slices whose fp32 products (twice the workspace) are added
- *     first;
+ *     more, 128 when Kr <= 128): one workgroup per (rank, tile of 128
+ *     channels x 64 or 128 tokens, or 256 x 256 when those fill whole rounds
+ *     of the 256 CUs) writes fp32 products Y[T,M,H] into the workspace, and a
+ *     streaming pass reduces them into out (the synced sum is the
+ *     ascending-rank fp32 sum of the per-rank products).  With at most 256
+ *     tiles of 128 x 64 and at least 16 chunks of 64 in each rank's
+ *     contraction, that contraction is cut in two slices whose fp32 products
+ *     (twice the workspace) are added first;
  *   - otherwise the fused tile kernel (each tile walks all T ranks), which
  *     needs no workspace.
  * caat_rowpar_pcr_fwd_workspace_bytes() gives the bytes a call needs (0:
@@ -114,17 +113,18 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  * products would exceed it cuts the contraction into fewer slices, or, if
  * even whole contractions do not fit, runs the path the shape would take
  * without the split (chunked decode or fused tiles); either gives the same
- * value up to fp32 summation order.  A decode call whose partials exceed it (e.g. T*H > 131056 channels
- * over all ranks at M = 32) returns CAAT_ERR_WORKSPACE before anything is
- * enqueued.  The scratch of the device current at the call is
- * used (`stream` must belong to it); its arrival counters are cleared by the
- * call itself (a small fill kernel, no memset).  Every call on one GPU shares
- * that GPU's scratch, so calls that may overlap on one GPU (different
- * streams, different threads) race and must be serialised by the caller.
- * Calls that need no workspace behave exactly like caat_rowpar_pcr_fwd, and
- * so do the others whose workspace fits the scratch.  Neither call allocates; this one calls no hipMalloc,
- * hipFree or allocating library routine at all.  CAAT_ERR_LAUNCH also covers
- * a failed lookup of the scratch's device address.
+ * value up to fp32 summation order.  A decode call whose partials exceed it
+ * (e.g. T*H > 131056 channels over all ranks at M = 32) returns
+ * CAAT_ERR_WORKSPACE before anything is enqueued.  The scratch of the device
+ * current at the call is used (`stream` must belong to it); its arrival
+ * counters are cleared by the call itself (a small fill kernel, no memset).
+ * Every call on one GPU shares that GPU's scratch, so calls that may overlap
+ * on one GPU (different streams, different threads) race and must be
+ * serialised by the caller.  Calls that need no workspace behave exactly like
+ * caat_rowpar_pcr_fwd, and so do the others whose workspace fits the
+ * scratch.  Neither call allocates; this one calls no hipMalloc, hipFree or
+ * allocating library routine at all.  CAAT_ERR_LAUNCH also covers a failed
+ * lookup of the scratch's device address.
  */
 #define CAAT_NOALLOC_SCRATCH_BYTES (16u << 20)
 int caat_rowpar_pcr_fwd_noalloc(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out,
