@@ -1,7 +1,8 @@
 """A seeded sweep of random shapes over every forward path (decode, chunked
-decode, split with 64- and 128-token tiles, fused 128x64 / 128x128 / 256x256
-tiles, the register-queue tiles) and the backward: integer inputs, bit for bit
-against the oracle, several ranks, ragged sizes, every kind of sync set."""
+decode, split with 128x64 tiles -- whole contractions or two slices of them --
+128x128 and 256x256 tiles, fused 128x64 / 128x128 / 256x256 tiles, the
+register-queue tiles) and the backward: integer inputs, bit for bit against the
+oracle, several ranks, ragged sizes, every kind of sync set."""
 import numpy as np
 import pytest
 import torch
