@@ -81,7 +81,8 @@ const char* caat_status_string(int status);
  *     3 * T * ceil(Kr/64) + 128 with T <= 8, 2 * T * ceil(Kr/64) + 64 with
  *     more, 128 when Kr <= 128): one workgroup per (rank, tile of 128
  *     channels x 64 or 128 tokens, or 256 x 256 when those fill whole rounds
- *     of the 256 CUs) writes fp32 products Y[T,M,H] into the workspace, and a
+ *     of the 256 CUs and their token blocks at least 3/4) writes fp32
+ *     products Y[T,M,H] into the workspace, and a
  *     streaming pass reduces them into out (the synced sum is the
  *     ascending-rank fp32 sum of the per-rank products).  With at most 256
  *     tiles of 128 x 64 and at least 16 chunks of 64 in each rank's

@@ -327,14 +327,17 @@ static int split_ks_rule(int T, int M, int Kr, int H) {
 // 57.8 / 109.0; 192 and 216 tiles (T = 4, M = 768; T = 8, Kr = 384, H = 768,
 // M = 2304): 60.3 / 39.9 -> 53.5 / 36.4.  Slower at 384 tiles (1.5 rounds:
 // +4 to +10%) and below 192 (+25 to +60%), and at T = 4, Kr = 1376, M = 960
-// (256 tiles): 64.4 -> 66.9.
+// (256 tiles): 64.4 -> 66.9.  Only with token tiles at least 3/4 full: at
+// T = 16, Kr = 688, M = 64 / 128 (256 tiles, a quarter / half full) they
+// took 32.5 / 38.9 us against 28.0 / 34.6 with 128 x 128 tiles.
 struct SplitPlan {
   int bm, bn, ks;
 };
 static SplitPlan split_plan(int T, int M, int Kr, int H) {
   const long long wg128 = (long long)T * ((H + 127) / 128) * ((M + 127) / 128);
-  const long long wg256 = (long long)T * ((H + 255) / 256) * ((M + 255) / 256);
-  if (wg256 % kCUs == 0 || (wg256 >= 192 && wg256 < kCUs)) return {256, 256, 1};
+  const long long tn256 = (M + 255) / 256, wg256 = (long long)T * ((H + 255) / 256) * tn256;
+  const bool full = 4LL * M >= 3LL * 256 * tn256;
+  if (full && (wg256 % kCUs == 0 || (wg256 >= 192 && wg256 < kCUs))) return {256, 256, 1};
   if (wg128 >= 512) return {128, 128, 1};
   return {128, 64, split_ks_rule(T, M, Kr, H)};
 }

@@ -14,7 +14,8 @@ def forward_path(T, M, Kr, H):
     limit = 128 if nk <= 2 else (3 * walk + 128 if T <= 8 else 2 * walk + 64)
     if T >= 2 and tiles64 <= limit:
         wg256 = T * -(-H // 256) * -(-M // 256)
-        if wg256 % 256 == 0 or 192 <= wg256 < 256:
+        full = 4 * M >= 3 * 256 * -(-M // 256)  # token tiles at least 3/4 full
+        if full and (wg256 % 256 == 0 or 192 <= wg256 < 256):
             return "split256"
         if T * -(-H // 128) * -(-M // 128) >= 512:
             return "split128"
