@@ -58,25 +58,29 @@ bool use_big_tiles(long long rows, long long cols, long long batch) {
   return ((rows + 255) / 256) * ((cols + 255) / 256) * batch >= 256;
 }
 
+// `mode` (FwdMode): every tile, or only those of the mask's uniform or mixed
+// 256-channel groups.
 template <int BM, int BN, int NW>
 int launch_fwd(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
-               int H, hipStream_t s) {
+               int H, hipStream_t s, int mode = kFwdAll) {
   const int tm = (H + BM - 1) / BM, tn = (M + BN - 1) / BN;  // channel tiles x token tiles
   hipLaunchKernelGGL((rowpar_pcr_fwd_kernel<BM, BN, NW>), dim3(tm * tn), dim3(NW * 64), 0, s, X, W, mask, out, T,
-                     M, Kr, H, tm, tn);
+                     M, Kr, H, tm, tn, mode);
   return launched();
 }
 
 // The forward with the earlier ranks' tiles held in registers (2 <= T <= 8).
 template <int BM, int BN, int NW>
 int launch_fwd_rb(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16_t* out, int T, int M, int Kr,
-                  int H, hipStream_t s) {
+                  int H, hipStream_t s, int mode = kFwdAll) {
   const int tm = (H + BM - 1) / BM, tn = (M + BN - 1) / BN;
   const dim3 grid(tm * tn), block(NW * 64);
   if (T <= 4)
-    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 4>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm, tn);
+    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 4>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm,
+                       tn, mode);
   else
-    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 8>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm, tn);
+    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 8>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm,
+                       tn, mode);
   return launched();
 }
 
@@ -427,24 +431,47 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
     }
     return CAAT_OK;
   }
-  if (use_big_tiles(M, H, 1)) return launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s);
   // Fewer than 512 tiles of 128 x 128 (two per CU): 64-token tiles give
   // twice as many workgroups (each walks all T ranks, so the tile count is
   // what fills the chip), up to three resident per CU.  Measured with the
   // same bits: 130M down-proj (384 tiles) 100 -> 91 us, out-proj 74 -> 68 us,
   // 7B down-proj at M = 1024 (256 tiles) 179 -> 154 us; at 512-1023 tiles the
   // 64-token tiles lose (M = 2048: 243 -> 321 us).
-  if ((long long)((H + 127) / 128) * ((M + 127) / 128) < 512) {
-    // The earlier ranks' tiles held in registers: with T <= 4 (three
-    // workgroups per CU still fit) and, at one per CU, for contractions of
-    // at most two chunks per rank.  Measured, same bits, M = 8192, H = 768,
-    // random S: Kr = 384, T = 2 22.5 -> 18.8 us, T = 4 45.3 -> 34.0 us;
-    // Kr = 96, T = 8 67.3 -> 61.0 us (at Kr = 384, T = 8 it loses, 93 -> 119).
-    if (mask != nullptr && T >= 2 && (T <= 4 || (T <= 8 && Kr <= 2 * kBK)))
-      return launch_fwd_rb<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
-    return launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
-  }
-  return launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s);
+  const bool small = !use_big_tiles(M, H, 1) && (long long)((H + 127) / 128) * ((M + 127) / 128) < 512;
+  // The earlier ranks' tiles held in registers, for every tile: with T <= 4
+  // (three workgroups per CU still fit) and, at two per CU, for contractions
+  // of at most two chunks per rank.  Measured, same bits, M = 8192, H = 768,
+  // random S: Kr = 384, T = 2 22.5 -> 18.8 us, T = 4 45.3 -> 34.0 us;
+  // Kr = 96, T = 8 67.3 -> 47 us.
+  if (small && mask != nullptr && T >= 2 && (T <= 4 || (T <= 8 && Kr <= 2 * kBK)))
+    return launch_fwd_rb<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s);
+  // With short contractions (at most six chunks per rank) and 2 <= T <= 8,
+  // the register-queue kernel takes the mask's mixed 256-channel groups (an
+  // 8-channel chunk with synced and local channels: the tiled kernels write
+  // those lines twice) and the tiled kernel the uniform ones, in two
+  // launches.  Measured at T = 8 with a random S (every group mixed), tiled
+  // -> register queue, us: Kr = 128, H = 2048, M = 8192 / 32768: 185 / 596
+  // -> 108 / 390; Kr = 256, H = 2048, M = 2048 / 8192 / 32768: 63 / 208 /
+  // 640 -> 42 / 145 / 581; Kr = 256, H = 4096, M = 2048 / 8192 / 16384: 98 /
+  // 396 / 679 -> 73 / 302 / 586; Kr = 192 / 384, H = 768, M = 16384: 138 /
+  // 172 -> 91 / 136.  With longer contractions the queue kernel loses at
+  // large M (Kr = 512, H = 4096, M = 16384: 831 -> 948; Kr = 704, H = 2048,
+  // M = 32768: 1091 -> 1566), and with a contiguous S (uniform groups) it
+  // loses too, so those keep the tiled kernels.  Where the 128 x 64 tiles
+  // run anyway, contractions of up to twelve chunks still gain (Kr = 512 /
+  // 704, H = 2048, M = 2048: 81 / 102 -> 60 / 81 us).
+  const int nkr = (Kr + kBK - 1) / kBK;
+  const bool dual = mask != nullptr && T >= 2 && T <= 8 && (nkr <= 6 || (small && nkr <= 12));
+  const int mode = dual ? kFwdUniform : kFwdAll;
+  int st;
+  if (use_big_tiles(M, H, 1))
+    st = launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s, mode);
+  else if (small)
+    st = launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s, mode);
+  else
+    st = launch_fwd<128, 128, 4>(X, W, mask, out, T, M, Kr, H, s, mode);
+  if (st != CAAT_OK || !dual) return st;
+  return launch_fwd_rb<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s, kFwdMixed);
 }
 
 // Shared by the row-parallel forward (mask = S) and the column-parallel

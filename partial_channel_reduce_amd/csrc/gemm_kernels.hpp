@@ -37,6 +37,35 @@ __device__ __forceinline__ unsigned long long uniform64(unsigned long long v) {
 // compiler from moving memory accesses across it).
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Which tiles a forward launch takes.  With a sync set that mixes synced and
+// local channels inside 8-channel chunks (a random or strided S), the tiled
+// kernel below writes those chunks twice (once at the rank's boundary, then
+// the synced sums as partial lines); the register-queue kernel writes them
+// once.  A launch can therefore be limited to the tiles whose 256-channel
+// group of the mask holds such a chunk (kFwdMixed) or holds none
+// (kFwdUniform), so that each kernel takes the groups it handles best.  The
+// results are the same bits either way.
+enum FwdMode { kFwdAll = 0, kFwdUniform = 1, kFwdMixed = 2 };
+
+// Whether the 256-channel group of channel c0 has an 8-channel chunk with
+// both synced and local channels (wave-uniform: all waves agree).
+__device__ __forceinline__ bool mask_group_mixed(const uint8_t* __restrict__ mask, int c0, int H, int lane) {
+  const int c = (c0 / kClassCols) * kClassCols + 8 * (lane & 31);
+  bool mixed = false;
+  if (lane < 32 && c < H) {  // H % 8 == 0: a chunk never straddles H
+    const u32x2 w = *reinterpret_cast<const u32x2*>(mask + c);
+    mixed = !(no_zero_byte(w[0]) && no_zero_byte(w[1])) && (w[0] | w[1]) != 0u;
+  }
+  return __any(mixed) != 0;
+}
+
+// Whether this workgroup's tile is outside the launch's share (all waves
+// agree, so the workgroup leaves together, before any barrier).
+__device__ __forceinline__ bool skip_tile(int mode, const uint8_t* __restrict__ mask, int c0, int H, int lane) {
+  if (mode == kFwdAll || mask == nullptr) return false;
+  return mask_group_mixed(mask, c0, H, lane) != (mode == kFwdMixed);
+}
+
 // ============================================================================
 // Forward.  (mask == nullptr: no channel is synced, i.e. T independent
 // products -- the column-parallel layer.)  One workgroup per (channel tile,
@@ -60,7 +89,7 @@ template <int BM, int BN, int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
 rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                       const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
-                      int T, int M, int Kr, int H, int tiles_m, int tiles_n) {
+                      int T, int M, int Kr, int H, int tiles_m, int tiles_n, int mode) {
   using S = TileShape<BM, BN, NW>;
   using RS = RowStage<S::WM>;
   constexpr int REG = S::BUF / NW;             // boundary staging per wave (elements)
@@ -75,6 +104,7 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, m0 = tn * BN;  // channel tile, token tile
+  if (skip_tile(mode, mask, c0, H, lane)) return;
   const int chw = c0 + wm * S::WM;       // this wave's first channel
   const int tkw = m0 + wn * S::WN;       // this wave's first token
   const int nk = (Kr + kBK - 1) / kBK;
@@ -253,7 +283,7 @@ template <int BM, int BN, int NW, int TB>
 __global__ void __launch_bounds__(NW * 64, TB > 4 ? 2 : 1)
 rowpar_pcr_fwd_rb_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out, int T, int M, int Kr, int H,
-                         int tiles_m, int tiles_n) {
+                         int tiles_m, int tiles_n, int mode) {
   using S = TileShape<BM, BN, NW>;
   using RS = RowStage<S::WM>;
   static_assert(TB >= 2 && TB <= 8, "ranks held in registers");
@@ -265,6 +295,7 @@ rowpar_pcr_fwd_rb_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int c0 = tm * BM, m0 = tn * BN;  // channel tile, token tile
+  if (skip_tile(mode, mask, c0, H, lane)) return;
   const int chw = c0 + wm * S::WM;       // this wave's first channel
   const int tkw = m0 + wn * S::WN;       // this wave's first token
   const int nk = (Kr + kBK - 1) / kBK;

@@ -23,11 +23,14 @@ def forward_path(T, M, Kr, H):
         return "split64x2" if tiles64 * T <= 256 and nk >= 16 else "split64"
     if M <= 192 and H <= 65536:
         return "chunked"
-    if -(-M // 256) * -(-H // 256) >= 256:
-        return "fused256"
-    if -(-H // 128) * -(-M // 128) < 512:
-        return "queue" if T >= 2 and (T <= 4 or (T <= 8 and Kr <= 128)) else "fused128x64"
-    return "fused128"
+    big = -(-M // 256) * -(-H // 256) >= 256
+    small = not big and -(-H // 128) * -(-M // 128) < 512
+    if small and T >= 2 and (T <= 4 or (T <= 8 and Kr <= 128)):
+        return "queue"
+    base = "fused256" if big else "fused128x64" if small else "fused128"
+    # short contractions: the mask's mixed 256-channel groups go to the
+    # register-queue kernel in a second launch
+    return base + "+queue" if 2 <= T <= 8 and (nk <= 6 or (small and nk <= 12)) else base
 
 
 def cases(n=64, seed=2026):
@@ -57,5 +60,10 @@ def cases(n=64, seed=2026):
             (8, 1800, 136, 768, "random", 0.5, 21), (8, 1900, 200, 776, "strided", 0.5, 22),
             (16, 2000, 72, 512, "random", 0.5, 23),
             # split forward, two contraction slices per rank (17 chunks: 9 + 8)
-            (4, 100, 1048, 512, "random", 0.5, 24)]
+            (4, 100, 1048, 512, "random", 0.5, 24),
+            # tiled forwards with more ranks than the register queue holds (one
+            # launch): 256x256 and 128x128 tiles; and 128x64 tiles with the
+            # mixed groups in a second launch
+            (9, 4096, 8, 4096, "random", 0.5, 25), (9, 2048, 16, 4096, "strided", 0.5, 26),
+            (8, 4096, 256, 512, "random", 0.5, 27)]
     return out

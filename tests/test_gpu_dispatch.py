@@ -50,15 +50,20 @@ def _tiles(rows, cols, tr, tc, batch=1):
 FWD_M = [32, 33, 192, 1024, 1025, 8064, 8065, 16128, 16129]
 
 
+# With a random S every 256-channel group of the mask is mixed, so past the
+# split range the register-queue kernel takes every tile (a one-chunk
+# contraction); with S = the first 512 channels every group is uniform and
+# the tiled kernels take them all.  Both sides of each switch run both ways.
+@pytest.mark.parametrize("kind", ["random", "prefix"])
 @pytest.mark.parametrize("M", FWD_M)
-def test_fwd_across_kernel_switch(ops, M):
+def test_fwd_across_kernel_switch(ops, M, kind):
     T, Kr, H = 2, 40, 1024
     assert _tiles(H, 1024, 128, 64) == 128 and _tiles(H, 1025, 128, 64) == 136
     assert _tiles(8064, H, 128, 128) == 504 and _tiles(8065, H, 128, 128) == 512
     assert _tiles(16128, H, 256, 256) == 252 and _tiles(16129, H, 256, 256) == 256
-    _announce(f"dispatch fwd T={T} M={M} Kr={Kr} H={H}")
+    _announce(f"dispatch fwd T={T} M={M} Kr={Kr} H={H} {kind}")
     X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=M, lo=-1, hi=1, x_zero_frac=0.4)
-    mask = synth.make_mask(H, 0.5, "random", seed=M + 1)
+    mask = synth.make_mask(H, 0.5, kind, seed=M + 1)
     ref = oracle.rowpar_pcr_fwd(X, W, mask)
     assert np.abs(ref).max() <= 256
     out = ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask))
