@@ -89,7 +89,11 @@ const char* caat_status_string(int status);
  *     contraction, that contraction is cut in two slices whose fp32 products
  *     (twice the workspace) are added first;
  *   - otherwise the fused tile kernel (each tile walks all T ranks), which
- *     needs no workspace.
+ *     needs no workspace.  With 2 <= T <= 8 and short contractions (at most
+ *     six chunks of 64 per rank, twelve with the smallest tiles) it runs in
+ *     two launches: 256-channel groups of the mask whose 8-channel chunks
+ *     mix synced and local channels go to a variant that holds the earlier
+ *     ranks' tiles in registers and writes each output line once.
  * caat_rowpar_pcr_fwd_workspace_bytes() gives the bytes a call needs (0:
  * pass NULL, 0).  The workspace starts with a 2 KiB region of 32-bit arrival
  * counters (the same size and place for every shape) that must be zero when
