@@ -50,6 +50,10 @@ constexpr int kBigTileWaves = 8;
 // Compute units of the MI355X: one round of one-per-CU workgroups.
 constexpr int kCUs = 256;
 
+// The fused forward's 256 x 256 tiles: from this many of them (see
+// fwd_launch).
+constexpr int kFwdBigTiles = 160;
+
 // 256 x 256 tiles (eight waves) when there are at least as many as CUs,
 // else 128 x 128 (four waves).  (At 256 to 511 big tiles, e.g. the weight
 // gradient of a 512-row out-projection shard, one big tile per CU beats four
@@ -437,7 +441,15 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   // same bits: 130M down-proj (384 tiles) 100 -> 91 us, out-proj 74 -> 68 us,
   // 7B down-proj at M = 1024 (256 tiles) 179 -> 154 us; at 512-1023 tiles the
   // 64-token tiles lose (M = 2048: 243 -> 321 us).
-  const bool small = !use_big_tiles(M, H, 1) && (long long)((H + 127) / 128) * ((M + 127) / 128) < 512;
+  // 256 x 256 tiles from 160 of them (5/8 of the CUs; the products need
+  // 256): measured, 128 x 128 -> 256 x 256 tiles, us: T = 8, Kr = 1376,
+  // H = 4096, M = 2560 / 3072 / 3584 / 3840 (160 / 192 / 224 / 240 tiles):
+  // 391 / 394 / 432 / 444 -> 345 / 345 / 370 / 386; T = 4, Kr = 2752,
+  // M = 2560 / 3584: 309 / 348 -> 259 / 301; T = 16, Kr = 688, M = 3584:
+  // 566 -> 500; Kr = 512 or 704: 2-7% faster.  With 128 of them they lose
+  // (T = 8, Kr = 1376, M = 2048: 235 -> 317).
+  const bool big = (long long)((M + 255) / 256) * ((H + 255) / 256) >= kFwdBigTiles;
+  const bool small = !big && (long long)((H + 127) / 128) * ((M + 127) / 128) < 512;
   // The earlier ranks' tiles held in registers, for every tile: with T <= 4
   // (three workgroups per CU still fit) and, at two per CU, for contractions
   // of at most two chunks per rank.  Measured, same bits, M = 8192, H = 768,
@@ -464,7 +476,7 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
   const bool dual = mask != nullptr && T >= 2 && T <= 8 && (nkr <= 6 || (small && nkr <= 12));
   const int mode = dual ? kFwdUniform : kFwdAll;
   int st;
-  if (use_big_tiles(M, H, 1))
+  if (big)
     st = launch_fwd<256, 256, kBigTileWaves>(X, W, mask, out, T, M, Kr, H, s, mode);
   else if (small)
     st = launch_fwd<128, 64, 4>(X, W, mask, out, T, M, Kr, H, s, mode);

@@ -23,7 +23,7 @@ def forward_path(T, M, Kr, H):
         return "split64x2" if tiles64 * T <= 256 and nk >= 16 else "split64"
     if M <= 192 and H <= 65536:
         return "chunked"
-    big = -(-M // 256) * -(-H // 256) >= 256
+    big = -(-M // 256) * -(-H // 256) >= 160
     small = not big and -(-H // 128) * -(-M // 128) < 512
     if small and T >= 2 and (T <= 4 or (T <= 8 and Kr <= 128)):
         return "queue"

@@ -1,13 +1,14 @@
 """GPU parity on both sides of every kernel-selection threshold.
 
 The library picks a kernel by problem size: the weight-streaming decode
-kernel up to 192 tokens, then GEMM tiles of 128x64, 128x128 or 256x256 by
-how many tiles the output has (too few to fill the chip's 256 CUs take the
-smaller tiles).  Each case here sits one token or eight channels below or
-above such a switch, so an off-by-one in the selection or in a kernel's
-edge handling shows up as a wrong element.  Integer-valued inputs keep every
-product and sum exact in bf16 and fp32, so the comparison with the oracle is
-bitwise."""
+kernel up to 32 tokens, the split forward while the fused tiles would be too
+few for their walk over the ranks, then fused tiles of 128x64, 128x128 or
+256x256 by how many tiles the output has (256x256 from 160 of them in the
+forward, from 256 in the backward's products).  Each case here sits one
+token or eight channels below or above such a switch, so an off-by-one in
+the selection or in a kernel's edge handling shows up as a wrong element.
+Integer-valued inputs keep every product and sum exact in bf16 and fp32, so
+the comparison with the oracle is bitwise."""
 import numpy as np
 import pytest
 import torch
@@ -46,8 +47,8 @@ def _tiles(rows, cols, tr, tc, batch=1):
 #   fused tiles of 128x64 for a walk of two chunks);  M = 1025 the first
 #   128x64-tile call;
 #   M = 8064 -> 504 tiles of 128x128 (still 128x64), M = 8065 -> 512 (128x128);
-#   M = 16128 -> 252 tiles of 256x256 (still 128x128), M = 16129 -> 256 (256x256).
-FWD_M = [32, 33, 192, 1024, 1025, 8064, 8065, 16128, 16129]
+#   M = 9984 -> 156 tiles of 256x256 (still 128x128), M = 9985 -> 160 (256x256).
+FWD_M = [32, 33, 192, 1024, 1025, 8064, 8065, 9984, 9985]
 
 
 # With a random S every 256-channel group of the mask is mixed, so past the
@@ -60,7 +61,7 @@ def test_fwd_across_kernel_switch(ops, M, kind):
     T, Kr, H = 2, 40, 1024
     assert _tiles(H, 1024, 128, 64) == 128 and _tiles(H, 1025, 128, 64) == 136
     assert _tiles(8064, H, 128, 128) == 504 and _tiles(8065, H, 128, 128) == 512
-    assert _tiles(16128, H, 256, 256) == 252 and _tiles(16129, H, 256, 256) == 256
+    assert _tiles(9984, H, 256, 256) == 156 and _tiles(9985, H, 256, 256) == 160
     _announce(f"dispatch fwd T={T} M={M} Kr={Kr} H={H} {kind}")
     X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=M, lo=-1, hi=1, x_zero_frac=0.4)
     mask = synth.make_mask(H, 0.5, kind, seed=M + 1)
