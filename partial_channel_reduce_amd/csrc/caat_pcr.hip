@@ -295,12 +295,23 @@ static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 //   T=8  Kr=384  H=768  (48): M = 1024 / 2304 / 3328: 45 / 50 / 58 -> 24 / 40 / 50
 //   T=8  Kr=96   H=768  (16): M = 1024 / 1600: 23 / 23 -> 21 / 29
 //   T=16 Kr=688  H=4096 (176): M = 256 / 512 / 960: 178 / 193 / 230 -> 87 / 148 / 242
-constexpr int kSplitMinM = kDecMaxM + 1;
+// Below that the weight-streaming kernel runs, from which the split takes
+// over at 16 tokens with T <= 4 (the streaming kernel's T x H/128
+// workgroups then leave most CUs idle), at 33 with 5 <= T <= 8 and at 24
+// with more ranks (its exchange grows with T x M).  Measured on MI355X,
+// H = 4096, random S, weights streamed from HBM, streaming -> split, us:
+// T = 2, Kr = 5504, M = 8 / 16 / 32: 40.0 / 42.2 / 48.4 -> 40.0 / 40.3 /
+// 40.9; T = 4, Kr = 2752, M = 8 / 16 / 32: 25.1 / 26.5 / 30.6 -> 25.3 /
+// 25.5 / 26.6; T = 16, Kr = 688, M = 16 / 24 / 32: 25.1 / 34.4 / 37.3 ->
+// 26.8 / 27.5 / 28.0; T = 8, Kr = 1376, M = 24 / 32: 22.7 / 23.5 -> 24.5 /
+// 25.0 (Kr = 512, M = 32: 15.6 -> 14.1; Kr = 256 or 704: the streaming
+// kernel or even).
+static int split_min_m(int T) { return T <= 4 ? 16 : T <= 8 ? kDecMaxM + 1 : 24; }
 static bool use_split(int T, int M, int Kr, int H) {
   const long long tiles = (long long)((H + 127) / 128) * ((M + 63) / 64);
   const long long nk = (Kr + kBK - 1) / kBK, walk = (long long)T * nk;
   const long long limit = nk <= 2 ? 128 : T <= 8 ? 3 * walk + 128 : 2 * walk + 64;
-  return T >= 2 && M >= kSplitMinM && tiles <= limit;
+  return T >= 2 && M >= split_min_m(T) && tiles <= limit;
 }
 
 // Slices of each rank's contraction in the split forward's 128 x 64 tiles:

@@ -6,13 +6,12 @@ import numpy as np
 
 def forward_path(T, M, Kr, H):
     """Which forward kernel the library runs for (T, M, Kr, H) with a mask."""
-    if M <= 32 and H <= 65536:
-        return "decode"
     tiles64 = -(-H // 128) * -(-M // 64)
     nk = -(-Kr // 64)
     walk = T * nk
     limit = 128 if nk <= 2 else (3 * walk + 128 if T <= 8 else 2 * walk + 64)
-    if T >= 2 and tiles64 <= limit:
+    min_m = 16 if T <= 4 else 33 if T <= 8 else 24  # where the split takes over from the decode kernel
+    if T >= 2 and M >= min_m and tiles64 <= limit:
         wg256 = T * -(-H // 256) * -(-M // 256)
         full = 4 * M >= 3 * 256 * -(-M // 256)  # token tiles at least 3/4 full
         if full and (wg256 % 256 == 0 or 192 <= wg256 < 256):
@@ -22,7 +21,7 @@ def forward_path(T, M, Kr, H):
         # two contraction slices per rank: few 128x64 tiles, long contractions
         return "split64x2" if tiles64 * T <= 256 and nk >= 16 else "split64"
     if M <= 192 and H <= 65536:
-        return "chunked"
+        return "decode" if M <= 32 else "chunked"
     big = -(-M // 256) * -(-H // 256) >= 160
     small = not big and -(-H // 128) * -(-M // 128) < 512
     if small and T >= 2 and (T <= 4 or (T <= 8 and Kr <= 128)):

@@ -144,7 +144,10 @@ INT_CASES = [
     (5, 7, 72, 136, "random", 0.25),     # decode path, ragged
     (1, 70, 64, 128, "random", 0.5),     # T = 1
     (20, 5, 64, 136, "random", 0.5),     # M <= 32, T = 20
-    (3, 17, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
+    (3, 15, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
+    (3, 16, 96, 72, "random", 0.5),      # split from 16 tokens with T <= 4, H not a multiple of 16
+    (16, 23, 40, 264, "strided", 0.5),   # decode, T = 16, the last size before the split
+    (16, 24, 40, 264, "strided", 0.5),   # split from 24 tokens with more than 8 ranks
     (1, 3, 64, 136, "random", 0.5),      # decode, T = 1 (every workgroup arrives last)
     (13, 17, 40, 264, "strided", 0.5),   # decode, T = 13, two token blocks
     (8, 1, 1376, 4096, "prefix", 0.5),   # decode: all-synced and all-local channel blocks
@@ -152,10 +155,11 @@ INT_CASES = [
     (4, 5, 64, 200, "prefix", 0.0),      # decode, nothing synced (no exchange), ragged block
     (4, 9, 64, 200, "prefix", 1.0),      # decode, everything synced, ragged block
     (13, 20, 40, 392, "prefix", 0.5),    # decode, T = 13, one mixed block between uniform ones
-    (8, 33, 1376, 512, "random", 0.5),   # decode in 32-token chunks: 32 + 1
-    (8, 100, 96, 264, "prefix", 0.5),    # chunks 32 + 32 + 32 + 4
-    (13, 70, 40, 136, "random", 0.5),    # chunks, T = 13
-    (4, 192, 64, 200, "strided", 0.5),   # the largest chunked M
+    (8, 33, 1376, 512, "random", 0.5),   # split from 33 tokens at T = 8 (two contraction slices)
+    (8, 100, 96, 264, "prefix", 0.5),    # split, 128 x 64 tiles
+    (13, 70, 40, 136, "random", 0.5),    # split, T = 13
+    (4, 192, 64, 200, "strided", 0.5),   # split, ragged channel block
+    (1, 192, 64, 200, "strided", 0.5),   # one rank: decode in 32-token chunks, the largest chunked M
 ]
 
 
