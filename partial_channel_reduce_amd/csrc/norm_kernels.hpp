@@ -20,7 +20,10 @@ constexpr int kNormMaxVecs = 4;  // 8-channel vectors per thread: H <= 8192
 // a butterfly across the wave read from lane 0, then the four waves in
 // order -- so every run gives the same bits.  R and Rout may be the same
 // array (in-place update of the residual stream): each element is read
-// before it is written, by the same thread.
+// before it is written, by the same thread.  Every load of the thread is
+// issued before its first store (the compiler may not move a load of R past
+// a store to Rout, which may alias it), and all four streams bypass the
+// caches' reuse (non-temporal): nothing here is read twice.
 template <int KV>
 __global__ void __launch_bounds__(kNormThreads)
 pcr_residual_rmsnorm_kernel(const uint16_t* __restrict__ Z, const uint16_t* R, const uint16_t* __restrict__ gamma,
@@ -28,13 +31,21 @@ pcr_residual_rmsnorm_kernel(const uint16_t* __restrict__ Z, const uint16_t* R, c
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hv = H / 8;
   const long long base = (long long)blockIdx.x * H;
-  u32x4 rn[KV];
+  u32x4 zv[KV], rn[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) {
+    const int v = tid + kNormThreads * i;
+    if (v < hv) {
+      zv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Z + base + v * 8));
+      rn[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R + base + v * 8));
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < KV; ++i) {
     const int v = tid + kNormThreads * i;
     if (v < hv) {
-      const u32x4 z = ld16(Z + base + v * 8), r = ld16(R + base + v * 8);
+      const u32x4 z = zv[i], r = rn[i];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const float lo = bf16_lo(z[d]) + bf16_lo(r[d]);
@@ -44,7 +55,7 @@ pcr_residual_rmsnorm_kernel(const uint16_t* __restrict__ Z, const uint16_t* R, c
         ss += a * a;
         ss += b * b;
       }
-      st16(Rout + base + v * 8, rn[i]);
+      st16_nt(Rout + base + v * 8, rn[i]);
     }
   }
 #pragma unroll
@@ -65,7 +76,7 @@ pcr_residual_rmsnorm_kernel(const uint16_t* __restrict__ Z, const uint16_t* R, c
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         o[d] = pack_bf16x2(bf16_lo(rn[i][d]) * scale * bf16_lo(g[d]), bf16_hi(rn[i][d]) * scale * bf16_hi(g[d]));
-      st16(N + base + v * 8, o);
+      st16_nt(N + base + v * 8, o);
     }
   }
 }
