@@ -73,10 +73,14 @@ const char* caat_status_string(int status);
  *   out[t][:, c] = Y_t[:, c]           for c not in S
  * rounded once to bf16 (nearest even).  `out` must not overlap X, W or mask.
  * Three kernels serve it, by shape:
- *   - few tokens (H <= 65536; M < 16 with T <= 4, M <= 32 with T <= 8,
- *     M < 24 with more ranks; with T = 1, M <= 192, 32 tokens at a time): a
- *     weight-streaming kernel whose workgroups exchange fp32 partials of the
- *     synced channels through the workspace;
+ *   - few tokens (H <= 65536; M <= 32 with T <= 8, M < 24 with more ranks;
+ *     with T = 1, M <= 192, 32 tokens at a time): a weight-streaming kernel
+ *     whose workgroups exchange fp32 partials of the synced channels through
+ *     the workspace.  With few ranks or channels each rank's contraction is
+ *     cut into ks slices of whole 32-row stages (ks doubled while
+ *     T * ks <= 8, T * ceil(H/128) * ks <= 256 and ceil(Kr/32) >= 16 * ks),
+ *     every slice's fp32 partials go through the workspace, and each rank's
+ *     value is its slices' sum in slice order;
  *   - from there on, T >= 2, while the fused kernel below would have few tiles for
  *     its walk over the ranks (ceil(H/128) * ceil(M/64) at most
  *     3 * T * ceil(Kr/64) + 128 with T <= 8, 2 * T * ceil(Kr/64) + 64 with

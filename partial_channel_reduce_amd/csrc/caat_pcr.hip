@@ -273,6 +273,26 @@ constexpr size_t kDecCounterBytes = (size_t)(kDecMaxH / kDecCols) * sizeof(int);
 static_assert(kDecCounterBytes % 256 == 0, "partials stay 256-byte aligned");
 static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 
+// Contraction slices per rank for the decode kernel: doubled while the
+// workgroups (T * H/128 * ks) stay within one per CU, T * ks <= 8 and every
+// wave keeps at least two 32-row stages of each slice.  So T * ks * H is at
+// most 32768 when ks > 1, and the sliced partials (ks * T * 32 * H fp32) take
+// at most 4 MiB.  Measured on MI355X (M = 1, weights streamed from HBM,
+// whole -> sliced, us): T = 1, Kr = 11008, H = 4096: 67.9 -> 20.0 (ks = 8);
+// T = 2, Kr = 5504: 38.4 -> 20.1 (4); T = 4, Kr = 2752: 24.2 -> 20.2 (2);
+// T = 2, Kr = 2816, H = 2048: 20.8 -> 11.7 (4); T = 4, Kr = 1024, H = 4096:
+// 12.1 -> 11.9 (2).  Two workgroups per CU, or one stage per wave, measured
+// the same.
+constexpr int kDecTargetWG = kCUs;
+static int dec_ks(int T, int Kr, int H) {
+  const int items = T * ((H + kDecCols - 1) / kDecCols);
+  const int ns = (Kr + kDecStage - 1) / kDecStage;
+  int ks = 1;
+  while (2 * ks <= kDecMaxKs && 2 * ks * T <= 8 && 2 * ks * items <= kDecTargetWG && ns >= 2 * ks * 2 * kDecWaves)
+    ks *= 2;
+  return ks;
+}
+
 // Token counts between decode and full tiles: the rank walk split across
 // workgroups, one per (rank, channel block, token block) with the tiles and
 // contraction slices of split_plan below, each writing its rank's fp32
@@ -295,18 +315,20 @@ static size_t decode_counter_bytes(int) { return kDecCounterBytes; }
 //   T=8  Kr=384  H=768  (48): M = 1024 / 2304 / 3328: 45 / 50 / 58 -> 24 / 40 / 50
 //   T=8  Kr=96   H=768  (16): M = 1024 / 1600: 23 / 23 -> 21 / 29
 //   T=16 Kr=688  H=4096 (176): M = 256 / 512 / 960: 178 / 193 / 230 -> 87 / 148 / 242
-// Below that the weight-streaming kernel runs, from which the split takes
-// over at 16 tokens with T <= 4 (the streaming kernel's T x H/128
-// workgroups then leave most CUs idle), at 33 with 5 <= T <= 8 and at 24
-// with more ranks (its exchange grows with T x M).  Measured on MI355X,
-// H = 4096, random S, weights streamed from HBM, streaming -> split, us:
-// T = 2, Kr = 5504, M = 8 / 16 / 32: 40.0 / 42.2 / 48.4 -> 40.0 / 40.3 /
-// 40.9; T = 4, Kr = 2752, M = 8 / 16 / 32: 25.1 / 26.5 / 30.6 -> 25.3 /
-// 25.5 / 26.6; T = 16, Kr = 688, M = 16 / 24 / 32: 25.1 / 34.4 / 37.3 ->
-// 26.8 / 27.5 / 28.0; T = 8, Kr = 1376, M = 24 / 32: 22.7 / 23.5 -> 24.5 /
-// 25.0 (Kr = 512, M = 32: 15.6 -> 14.1; Kr = 256 or 704: the streaming
-// kernel or even).
-static int split_min_m(int T) { return T <= 4 ? 16 : T <= 8 ? kDecMaxM + 1 : 24; }
+// Below that the weight-streaming kernel runs (with few ranks in contraction
+// slices), up to its 32-token limit with T <= 8; with more ranks (no slices,
+// and its exchange grows with T x M) the split takes over at 24 tokens.
+// Measured on MI355X, random S, weights streamed from HBM, split ->
+// streaming, us: T = 2, Kr = 5504, H = 4096, M = 16 / 32: 40.5 / 40.6 ->
+// 21.2 / 24.4; T = 2, Kr = 512: 13.1 / 12.5 -> 9.7 / 9.8; T = 3, Kr = 2000,
+// H = 2048: 19.5 / 20.2 -> 13.3 / 16.3; T = 4, Kr = 2752: 25.6 / 26.2 ->
+// 21.3 / 25.1; T = 2, Kr = 5504, H = 16384: 65.9 / 68.0 -> 61.8 / 63.4.  The
+// split wins by 1-2 us at T = 4 from 20 or 28 tokens with short
+// contractions (Kr = 1024, H = 4096, M = 32: 14.1 -> 16.1; Kr = 1408,
+// H = 2048: 14.9 -> 16.1).  T = 16, Kr = 688, H = 4096, streaming -> split:
+// M = 16 / 24 / 32: 25.1 / 34.4 / 37.3 -> 26.8 / 27.5 / 28.0; T = 8,
+// Kr = 1376, M = 24 / 32: 22.7 / 23.5 -> 24.5 / 25.0.
+static int split_min_m(int T) { return T <= 8 ? kDecMaxM + 1 : 24; }
 static bool use_split(int T, int M, int Kr, int H) {
   const long long tiles = (long long)((H + 127) / 128) * ((M + 63) / 64);
   const long long nk = (Kr + kBK - 1) / kBK, walk = (long long)T * nk;
@@ -371,7 +393,8 @@ static size_t fwd_need(int T, int M, int Kr, int H, int split) {
     return kDecCounterBytes + round256((size_t)ks * T * M * H * sizeof(float));
   }
   if (!use_decode(M, H)) return 0;
-  return decode_counter_bytes(H) + round256((size_t)T * (M < kDecMaxM ? M : kDecMaxM) * H * sizeof(float));
+  return decode_counter_bytes(H) +
+         round256((size_t)dec_ks(T, Kr, H) * T * (M < kDecMaxM ? M : kDecMaxM) * H * sizeof(float));
 }
 
 size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H) {
@@ -428,7 +451,8 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
     int* arrivals = static_cast<int*>(workspace);
     float* partial =
         workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(H)) : nullptr;
-    const dim3 grid(((H + kDecCols - 1) / kDecCols) * T);
+    const int ks = partial ? dec_ks(T, Kr, H) : 1;  // no workspace (no mask): whole contractions
+    const dim3 grid(((H + kDecCols - 1) / kDecCols) * T * ks);
     const long long xs = (long long)M * Kr, os = (long long)M * H;  // rank strides of X and out
     // Chunks run one after another on the stream and share the workspace;
     // each launch leaves the arrival counters at zero for the next.
@@ -436,12 +460,18 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
       const int mc = M - m0 < kDecMaxM ? M - m0 : kDecMaxM;
       const uint16_t* Xc = X + (long long)m0 * Kr;
       uint16_t* oc = out + (long long)m0 * H;
-      if (mc <= 16)
-        hipLaunchKernelGGL(rowpar_pcr_decode_kernel<1>, grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc, partial,
-                           arrivals, T, mc, Kr, H, xs, os);
+      if (mc <= 16 && ks == 1)
+        hipLaunchKernelGGL((rowpar_pcr_decode_kernel<1, false>), grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc,
+                           partial, arrivals, T, mc, Kr, H, xs, os, ks);
+      else if (mc <= 16)
+        hipLaunchKernelGGL((rowpar_pcr_decode_kernel<1, true>), grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc,
+                           partial, arrivals, T, mc, Kr, H, xs, os, ks);
+      else if (ks == 1)
+        hipLaunchKernelGGL((rowpar_pcr_decode_kernel<2, false>), grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc,
+                           partial, arrivals, T, mc, Kr, H, xs, os, ks);
       else
-        hipLaunchKernelGGL(rowpar_pcr_decode_kernel<2>, grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc, partial,
-                           arrivals, T, mc, Kr, H, xs, os);
+        hipLaunchKernelGGL((rowpar_pcr_decode_kernel<2, true>), grid, dim3(kDecThreads), 0, s, Xc, W, mask, oc,
+                           partial, arrivals, T, mc, Kr, H, xs, os, ks);
       if (int st = launched()) return st;
     }
     return CAAT_OK;

@@ -19,6 +19,12 @@
 //     synced values in ascending rank order and writes every rank's output
 //     (the one bf16 sum on synced channels, the rank's own value elsewhere)
 //     with whole 8-byte stores.
+//   With few ranks or channel blocks (T * H/128 workgroups would leave CUs
+//     idle) each rank's contraction is cut into ks slices of whole 32-row
+//     stages, one workgroup each (T * ks <= 8).  Every block then goes
+//     through the exchange: the last of its T * ks workgroups adds each
+//     rank's slices in slice order, then the synced channels over the ranks
+//     in ascending order.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -26,6 +32,7 @@
 namespace caat {
 
 constexpr int kDecMaxM = 32;     // two 16-row MFMA blocks per launch
+constexpr int kDecMaxKs = 8;     // contraction slices per rank: T * ks <= 8
 constexpr int kDecChunkedMaxM = 192;  // larger M up to this: one launch per 32-token chunk
 constexpr int kDecCols = 128;    // channels per workgroup: 256 bytes of each weight row
 constexpr int kDecWaves = 8;
@@ -48,13 +55,16 @@ __device__ __forceinline__ int dec_off(int k, int ch) {
 // NB: MFMA row blocks of 16 tokens, 1 (M <= 16) or 2.  The M token rows of
 // rank t start at X + t * xs and out + t * os (xs = M * Kr and os = M * H
 // for a whole call; larger when the call is one 32-token chunk of a bigger
-// batch, X and out then pointing at the chunk's first row).
-template <int NB>
+// batch, X and out then pointing at the chunk's first row).  SL: the
+// contraction may come in ks > 1 slices (without it ks is taken as 1 and the
+// slice arithmetic compiles away).
+template <int NB, bool SL>
 __global__ void __launch_bounds__(kDecThreads)
 rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                          float* __restrict__ partial, int* __restrict__ arrivals, int T, int M, int Kr,
-                         int H, long long xs, long long os) {
+                         int H, long long xs, long long os, int ks_arg) {
+  const int ks = SL ? ks_arg : 1;
   constexpr int D = 2;                      // stages held in registers: one being used, one loading
   constexpr int SE = kDecStage * kDecCols;  // W elements per stage (4 KiB)
   constexpr int SLOT = SE;                  // one LDS slot per wave
@@ -66,18 +76,23 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = (H + kDecCols - 1) / kDecCols;
-  // Each XCD takes a contiguous range of (rank, channel block) items, so with
-  // T = 8 every XCD serves one rank and its L2 reads that rank's tokens once
-  // (numbered rank-major, each rank's blocks would be spread over all eight).
+  // Each XCD takes a contiguous range of (rank, channel block, slice) items,
+  // so with T = 8 every XCD serves one rank and its L2 reads that rank's
+  // tokens once (numbered rank-major, each rank's blocks would be spread over
+  // all eight).
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = lin / nb;
-  const int n0 = (lin - t * nb) * kDecCols;
+  const int per = nb * ks;
+  const int t = lin / per;
+  const int blk = (lin - t * per) / ks, sl = lin - t * per - blk * ks;
+  const int n0 = blk * kDecCols;
   const long long MK = (long long)M * Kr, KH = (long long)Kr * H, MH = (long long)M * H;
 
-  // This wave's share of the contraction: 32-row stages wave, wave + 4,
-  // wave + 8, ... (the workgroup's waves read adjacent row groups together).
+  // This workgroup's slice: 32-row stages [s_lo, s_hi) of the rank's
+  // contraction; this wave's share of it: stages s_lo + wave, s_lo + wave + 8,
+  // ... (the workgroup's waves read adjacent row groups together).
   const int ns_all = (Kr + kDecStage - 1) / kDecStage;
-  const int nst = (ns_all - wave + kDecWaves - 1) / kDecWaves;
+  const int s_lo = sl * ns_all / ks, s_hi = (sl + 1) * ns_all / ks;
+  const int nst = (s_hi - s_lo - wave + kDecWaves - 1) / kDecWaves;
 
   // Operands are loaded into registers D-1 stages ahead (plain buffer loads:
   // the compiler tracks them and waits exactly).  Per lane and stage: 8
@@ -103,7 +118,7 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   constexpr int kNt = 1 << 1;  // weights are read once: non-temporal (streaming) loads
   auto load = [&](int st, Stage& S) {
     const bool live = st < nst;
-    const int k0 = (st * kDecWaves + wave) * kDecStage;
+    const int k0 = (s_lo + st * kDecWaves + wave) * kDecStage;
 #pragma unroll
     for (int i = 0; i < kDecLoads; ++i)
       S.w[i] = __builtin_bit_cast(
@@ -213,8 +228,9 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   };
   // A channel block without synced channels (the same for all T workgroups
   // of the block; every block when mask == nullptr) needs no exchange and
-  // no workspace: each rank writes its own values.
-  if (!__syncthreads_or(mbits != 0u)) {
+  // no workspace when the contraction is whole: each rank writes its own
+  // values.
+  if (ks == 1 && !__syncthreads_or(mbits != 0u)) {
     if (inb)
 #pragma unroll
       for (int p = 0; p < NP; ++p)
@@ -240,9 +256,10 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   // M = 1 / 8 / 32 took 21.5 / 23.1 / 28.2 us against 18.8 / 19.3 / 23.0.  The bitwise decode
   // tests (chunked calls, a shared workspace, graph replays) guard it.
   constexpr int kSc1 = 1 << 4;
+  // Slice sl of rank u sits at partial + (sl * T + u) * M * H.
   auto prs = [&](int u) { return make_rsrc(partial + u * MH, (uint32_t)(MH * 4)); };
   if (inb) {
-    const __amdgpu_buffer_rsrc_t r = prs(t);
+    const __amdgpu_buffer_rsrc_t r = prs(sl * T + t);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int m = mt + RPP * p;
@@ -252,8 +269,8 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   __shared__ int is_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const int blk = lin - t * nb;
-  if (tid == 0) is_last = __hip_atomic_fetch_add(arrivals + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == T - 1;
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(arrivals + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == T * ks - 1;
   __syncthreads();
   if (!is_last) return;
   if (tid == 0) __hip_atomic_store(arrivals + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -266,6 +283,44 @@ rowpar_pcr_decode_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
     for (int e = 0; e < 4; ++e) r[e] = syn[e] ? a[e] : b[e];
     return r;
   };
+  if (SL && ks > 1) {
+    // T * ks <= 8: every slice of every rank in flight together; each rank's
+    // value is its slices' sum in slice order.
+    const int n = T * ks;
+    f32x4_t v[NP][8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < n) {
+        const __amdgpu_buffer_rsrc_t r = prs(k);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int m = mt + RPP * p;
+          if (m < M) v[p][k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (m * H + c4) * 4, 0, kSc1));
+        }
+      }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int m = mt + RPP * p;
+      if (m >= M) continue;
+      f32x4_t vr[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < T) {
+          vr[u] = v[p][u];
+#pragma unroll
+          for (int k = u + 1; k < 8; ++k)  // k = q * T + u: slices q = 1 .. ks - 1, in order
+            if (k < n && (k - u) % T == 0) vr[u] += v[p][k];
+        }
+      f32x4_t sum = vr[0];
+#pragma unroll
+      for (int u = 1; u < 8; ++u)
+        if (u < T) sum += vr[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < T) put(u, m, sel(sum, vr[u]));
+    }
+    return;
+  }
   for (int u0 = 0; u0 < T; u0 += 8) {
     f32x4_t v[NP][8];
 #pragma unroll

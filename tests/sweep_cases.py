@@ -4,13 +4,23 @@ that every path is covered)."""
 import numpy as np
 
 
+def decode_slices(T, Kr, H):
+    """Contraction slices per rank the decode kernel takes (whole stages of 32
+    rows): doubled while T * ks <= 8, the workgroups T * ceil(H/128) * ks stay
+    within 256 and each of the 8 waves keeps two stages of every slice."""
+    items, ns, ks = T * -(-H // 128), -(-Kr // 32), 1
+    while 2 * ks <= 8 and 2 * ks * T <= 8 and 2 * ks * items <= 256 and ns >= 2 * ks * 16:
+        ks *= 2
+    return ks
+
+
 def forward_path(T, M, Kr, H):
     """Which forward kernel the library runs for (T, M, Kr, H) with a mask."""
     tiles64 = -(-H // 128) * -(-M // 64)
     nk = -(-Kr // 64)
     walk = T * nk
     limit = 128 if nk <= 2 else (3 * walk + 128 if T <= 8 else 2 * walk + 64)
-    min_m = 16 if T <= 4 else 33 if T <= 8 else 24  # where the split takes over from the decode kernel
+    min_m = 33 if T <= 8 else 24  # where the split takes over from the decode kernel
     if T >= 2 and M >= min_m and tiles64 <= limit:
         wg256 = T * -(-H // 256) * -(-M // 256)
         full = 4 * M >= 3 * 256 * -(-M // 256)  # token tiles at least 3/4 full
@@ -21,7 +31,8 @@ def forward_path(T, M, Kr, H):
         # two contraction slices per rank: few 128x64 tiles, long contractions
         return "split64x2" if tiles64 * T <= 256 and nk >= 16 else "split64"
     if M <= 192 and H <= 65536:
-        return "decode" if M <= 32 else "chunked"
+        base = "decode" if M <= 32 else "chunked"
+        return base + "_sliced" if decode_slices(T, Kr, H) > 1 else base
     big = -(-M // 256) * -(-H // 256) >= 160
     small = not big and -(-H // 128) * -(-M // 128) < 512
     if small and T >= 2 and (T <= 4 or (T <= 8 and Kr <= 128)):
@@ -64,5 +75,9 @@ def cases(n=64, seed=2026):
             # launch): 256x256 and 128x128 tiles; and 128x64 tiles with the
             # mixed groups in a second launch
             (9, 4096, 8, 4096, "random", 0.5, 25), (9, 2048, 16, 4096, "strided", 0.5, 26),
-            (8, 4096, 256, 512, "random", 0.5, 27)]
+            (8, 4096, 256, 512, "random", 0.5, 27),
+            # decode with contraction slices: 8 (one rank), 4 (two ranks, ragged
+            # channel block), 2 (three ranks); one rank in 32-token chunks
+            (1, 3, 4104, 520, "random", 0.5, 28), (2, 9, 2056, 776, "prefix", 0.5, 29),
+            (3, 7, 2000, 264, "strided", 0.5, 30), (1, 70, 1032, 264, "random", 0.5, 31)]
     return out

@@ -139,7 +139,8 @@ def test_workspace_sizes(L):
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(16, 833, 688, H) == 0
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 256, 96, 768) == 2048 + T * 256 * 768 * 4  # 24 tiles
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(T, 1408, 96, 768) == 0  # 132 tiles, two-chunk walk: fused
-    assert L.caat_rowpar_pcr_fwd_workspace_bytes(1, 100, Kr, H) == 2048 + 32 * H * 4  # one rank: chunked decode
+    # one rank: chunked decode, 43 stages of 32 rows in two contraction slices
+    assert L.caat_rowpar_pcr_fwd_workspace_bytes(1, 100, Kr, H) == 2048 + 2 * 32 * H * 4
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65536) == 2048 + 2 * 8 * 65536 * 4
     assert L.caat_rowpar_pcr_fwd_workspace_bytes(2, 8, 64, 65544) == 0  # above 65536 channels: tiled
     for M in (1, 8, 32):
@@ -152,6 +153,25 @@ def test_workspace_sizes(L):
     assert L.caat_pcr_bwd_workspace_bytes(T, 16384, Kr, H) % 256 == 0
     assert L.caat_pcr_bwd_workspace_bytes(T, 0, Kr, H) == 0
     assert L.caat_pcr_bwd_workspace_bytes(0, 8, Kr, H) == 0  # invalid dims report 0
+
+
+def test_decode_slice_workspace(L):
+    """Below the split forward's start, few ranks cut each contraction into ks
+    slices (T * ks <= 8, at most 256 workgroups of 128 channels, two 32-row
+    stages per wave and slice); the workspace holds every slice's partials."""
+    H = 4096
+    ws = L.caat_rowpar_pcr_fwd_workspace_bytes
+    assert ws(1, 8, 11008, H) == 2048 + 8 * 1 * 8 * H * 4   # 344 stages: 8 slices
+    assert ws(1, 8, 4096, H) == 2048 + 8 * 1 * 8 * H * 4    # 128 stages: still 8
+    assert ws(1, 8, 4064, H) == 2048 + 4 * 1 * 8 * H * 4    # 127 stages: 4
+    assert ws(2, 15, 5504, H) == 2048 + 4 * 2 * 15 * H * 4  # T * ks <= 8
+    assert ws(4, 8, 2752, H) == 2048 + 2 * 4 * 8 * H * 4
+    assert ws(4, 8, 1024, H) == 2048 + 2 * 4 * 8 * H * 4    # 32 stages: two slices of 16
+    assert ws(4, 8, 992, H) == 2048 + 4 * 8 * H * 4         # 31 stages: whole
+    assert ws(8, 8, 11008, H) == 2048 + 8 * 8 * H * 4       # eight ranks: whole
+    assert ws(2, 8, 5504, 16384) == 2048 + 2 * 8 * 16384 * 4  # 256 blocks already
+    assert ws(2, 8, 5504, 8192) == 2048 + 2 * 2 * 8 * 8192 * 4  # 128 blocks: two slices
+    assert ws(3, 7, 2000, 264) == 2048 + -(-2 * 3 * 7 * 264 * 4 // 256) * 256  # 63 stages, T = 3: two slices
 
 
 def test_bwd_workspace_split_pieces(L):

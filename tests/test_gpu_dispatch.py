@@ -43,12 +43,12 @@ def _tiles(rows, cols, tr, tc, batch=1):
 
 
 # Forward, T = 2 ranks, Kr = 40, H = 1024 channels (8 tiles of 128, 4 of 256):
-#   M <= 15 decode;  16 <= M <= 1024 the split forward (from 16 tokens with
-#   T <= 4; at most 128 fused tiles of 128x64 for a walk of two chunks);
+#   M <= 32 decode;  33 <= M <= 1024 the split forward (at most 128 fused
+#   tiles of 128x64 for a walk of two chunks);
 #   M = 1025 the first 128x64-tile call;
 #   M = 8064 -> 504 tiles of 128x128 (still 128x64), M = 8065 -> 512 (128x128);
 #   M = 9984 -> 156 tiles of 256x256 (still 128x128), M = 9985 -> 160 (256x256).
-FWD_M = [15, 16, 32, 33, 192, 1024, 1025, 8064, 8065, 9984, 9985]
+FWD_M = [32, 33, 192, 1024, 1025, 8064, 8065, 9984, 9985]
 
 
 # With a random S every 256-channel group of the mask is mixed, so past the

@@ -144,8 +144,7 @@ INT_CASES = [
     (5, 7, 72, 136, "random", 0.25),     # decode path, ragged
     (1, 70, 64, 128, "random", 0.5),     # T = 1
     (20, 5, 64, 136, "random", 0.5),     # M <= 32, T = 20
-    (3, 15, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
-    (3, 16, 96, 72, "random", 0.5),      # split from 16 tokens with T <= 4, H not a multiple of 16
+    (3, 17, 96, 72, "random", 0.5),      # decode, H not a multiple of 16
     (16, 23, 40, 264, "strided", 0.5),   # decode, T = 16, the last size before the split
     (16, 24, 40, 264, "strided", 0.5),   # split from 24 tokens with more than 8 ranks
     (1, 3, 64, 136, "random", 0.5),      # decode, T = 1 (every workgroup arrives last)

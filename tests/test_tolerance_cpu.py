@@ -110,5 +110,5 @@ def test_sweep_covers_every_forward_path():
     from tests.sweep_cases import cases, forward_path
 
     paths = {forward_path(*c[:4]) for c in cases()}
-    assert paths >= {"decode", "chunked", "split64", "split64x2", "split128", "split256", "fused128x64", "fused128", "fused256", "queue",
+    assert paths >= {"decode", "chunked", "decode_sliced", "chunked_sliced", "split64", "split64x2", "split128", "split256", "fused128x64", "fused128", "fused256", "queue",
                      "fused256+queue", "fused128+queue", "fused128x64+queue"}, paths
