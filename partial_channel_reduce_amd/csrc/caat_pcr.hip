@@ -211,6 +211,7 @@ int launch_reduce_f32_bf16(const float* y, const uint8_t* mask, uint16_t* o, int
     case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
     case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
     case 8: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
+    case 16: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
     default: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
   }
   return launched();
@@ -231,6 +232,7 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
     case 2: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
     case 4: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
     case 8: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
+    case 16: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
     default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
   }
   return launched();
@@ -759,6 +761,7 @@ int caat_partial_channel_reduce(const void* Y, const uint8_t* mask, void* out, i
       case 2: hipLaunchKernelGGL(pcr_reduce_f32_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
       case 4: hipLaunchKernelGGL(pcr_reduce_f32_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
       case 8: hipLaunchKernelGGL(pcr_reduce_f32_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
+      case 16: hipLaunchKernelGGL(pcr_reduce_f32_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
       default: hipLaunchKernelGGL(pcr_reduce_f32_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf); break;
     }
   } else {

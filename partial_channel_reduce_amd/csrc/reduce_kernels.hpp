@@ -31,7 +31,7 @@ __device__ __forceinline__ uint32_t reduce_block(uint32_t groups) {
 // with only local channels still loads and stores its T vectors), so no lane
 // serialises the wave's loads behind a divergent branch.  In place, lanes with
 // no synced channel leave at once, and mixed vectors write synced channels only.
-template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
+template <int TC>  // TC = T known at compile time (1..16), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* out,
                       int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace,
@@ -74,24 +74,41 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
     }
   } else {
     // Runtime T: first pass sums, second pass writes (re-reading rank t's
-    // vector for the local channels).
-    f32x4 s = *reinterpret_cast<const f32x4*>(Y + base);
-    for (int t = 1; t < T; ++t) s += *reinterpret_cast<const f32x4*>(Y + t * mh + base);
-    for (int t = 0; t < T; ++t) {
-      float* o = out + t * mh + base;
-      if (!inplace || all) {
-        const f32x4 y = *reinterpret_cast<const f32x4*>(Y + t * mh + base);
-        f32x4 w;
-        w.x = s0 ? s.x : y.x;
-        w.y = s1 ? s.y : y.y;
-        w.z = s2 ? s.z : y.z;
-        w.w = s3 ? s.w : y.w;
-        __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(o));
-      } else {
-        if (s0) o[0] = s.x;
-        if (s1) o[1] = s.y;
-        if (s2) o[2] = s.z;
-        if (s3) o[3] = s.w;
+    // vector for the local channels); both take the ranks eight at a time
+    // with the group's loads in flight together.
+    f32x4 s;
+    for (int t0 = 0; t0 < T; t0 += 8) {
+      f32x4 g[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) g[k] = *reinterpret_cast<const f32x4*>(Y + (t0 + k) * mh + base);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) s = t0 + k == 0 ? g[k] : s + g[k];
+    }
+    for (int t0 = 0; t0 < T; t0 += 8) {
+      f32x4 g[8];
+      if (!inplace || all)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (t0 + k < T) g[k] = *reinterpret_cast<const f32x4*>(Y + (t0 + k) * mh + base);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (t0 + k >= T) break;
+        float* o = out + (t0 + k) * mh + base;
+        if (!inplace || all) {
+          f32x4 w;
+          w.x = s0 ? s.x : g[k].x;
+          w.y = s1 ? s.y : g[k].y;
+          w.z = s2 ? s.z : g[k].z;
+          w.w = s3 ? s.w : g[k].w;
+          __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(o));
+        } else {
+          if (s0) o[0] = s.x;
+          if (s1) o[1] = s.y;
+          if (s2) o[2] = s.z;
+          if (s3) o[3] = s.w;
+        }
       }
     }
   }
@@ -104,7 +121,7 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
 // and T 8-byte stores.  With ks > 1 the products come in ks contraction
 // slices, Y[q][t] at Y + q * sstride + t * mh, and rank t's value is their
 // fp32 sum in slice order.
-template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
+template <int TC>  // TC = T known at compile time (1..16), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                            int T_rt, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups, int ks,
@@ -120,11 +137,16 @@ pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restric
   const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
   // Runtime T: a rank's product (its slices in slice order) is read twice,
   // for the sum and for the output, with plain loads so the second read
-  // finds the lines in cache.
-  auto rank_value = [&](int t) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(Y + t * mh + base);
-    for (int q = 1; q < ks; ++q) a += *reinterpret_cast<const f32x4*>(Y + q * sstride + t * mh + base);
-    return a;
+  // finds the lines in cache; ranks go eight at a time, the group's loads in
+  // flight together.
+  auto rank_group = [&](int t0, f32x4 (&g)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (t0 + k < T) g[k] = *reinterpret_cast<const f32x4*>(Y + (t0 + k) * mh + base);
+    for (int q = 1; q < ks; ++q)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) g[k] += *reinterpret_cast<const f32x4*>(Y + q * sstride + (t0 + k) * mh + base);
   };
   f32x4 y[NR];
   f32x4 s;
@@ -139,16 +161,31 @@ pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restric
 #pragma unroll
     for (int t = 1; t < NR; ++t) s += y[t];
   } else {
-    s = rank_value(0);
-    for (int t = 1; t < T; ++t) s += rank_value(t);
+    for (int t0 = 0; t0 < T; t0 += 8) {
+      f32x4 g[8];
+      rank_group(t0, g);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) s = t0 + k == 0 ? g[k] : s + g[k];
+    }
   }
-#pragma unroll 8
-  for (int t = 0; t < T; ++t) {
-    const f32x4 yt = TC > 0 ? y[t < NR ? t : 0] : rank_value(t);
+  auto put = [&](int t, f32x4 yt) {
     u32x2 o;
     o[0] = pack_bf16x2(s0 ? s.x : yt.x, s1 ? s.y : yt.y);
     o[1] = pack_bf16x2(s2 ? s.z : yt.z, s3 ? s.w : yt.w);
     __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * mh + base));
+  };
+  if constexpr (TC > 0) {
+#pragma unroll
+    for (int t = 0; t < NR; ++t) put(t, y[t]);
+  } else {
+    for (int t0 = 0; t0 < T; t0 += 8) {
+      f32x4 g[8];
+      rank_group(t0, g);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) put(t0 + k, g[k]);
+    }
   }
 }
 
@@ -206,7 +243,7 @@ __device__ __forceinline__ u32x4 expand_mask8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-template <int TC>  // TC = T known at compile time (1..8), or 0 for a runtime T
+template <int TC>  // TC = T known at compile time (1..16), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint16_t* out,
                        int T_rt, uint32_t nvec, uint32_t hvec, long long mh, int inplace,
@@ -244,27 +281,51 @@ pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint
       for (int e = 0; e < 8; ++e) s[e] += f[e];
     }
   } else {
-    bf16x8_to_f32(ld16(Y + base), s);
-    for (int t = 1; t < T; ++t) {
-      float f[8];
-      bf16x8_to_f32(ld16(Y + t * mh + base), f);
+    // Runtime T: ranks eight at a time, the group's loads in flight together.
+    for (int t0 = 0; t0 < T; t0 += 8) {
+      u32x4 g[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] += f[e];
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) g[k] = ld16(Y + (t0 + k) * mh + base);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < T) {
+          float f[8];
+          bf16x8_to_f32(g[k], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] = t0 + k == 0 ? f[e] : s[e] + f[e];
+        }
     }
   }
   u32x4 sv;
 #pragma unroll
   for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
-#pragma unroll 8
-  for (int t = 0; t < ranks_out; ++t) {
+  auto put = [&](int t, u32x4 yt) {
     uint16_t* o = out + t * mh + base;
     if (!inplace || all) {
-      const u32x4 yt = TC > 0 ? y[t < NR ? t : 0] : ld16(Y + t * mh + base);
       st16_nt(o, (sv & sel) | (yt & ~sel));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if ((sel[e >> 1] >> (16 * (e & 1))) & 1u) o[e] = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
+    }
+  };
+  if constexpr (TC > 0) {
+#pragma unroll
+    for (int t = 0; t < NR; ++t)
+      if (t < ranks_out) put(t, y[t]);
+  } else {
+    // Every load of a group goes out before its first store (each element is
+    // still read before it is written, by the same thread, in place too).
+    for (int t0 = 0; t0 < ranks_out; t0 += 8) {
+      u32x4 g[8];
+      if (!inplace || all)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (t0 + k < ranks_out) g[k] = ld16(Y + (t0 + k) * mh + base);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + k < ranks_out) put(t0 + k, g[k]);
     }
   }
 }
