@@ -141,20 +141,25 @@ pcr_reduce_residual_rmsnorm_kernel(const uint16_t* __restrict__ Y, const uint8_t
       }
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < KV; ++i) {
-      const int v = tid + kNormThreads * i;
-      if (v < hv) bf16x8_to_f32(ld16(Y + row + v * 8), sacc[i]);
-    }
-    for (int t = 1; t < T; ++t)
+    // Ranks eight at a time, every load of a group in flight together; the
+    // sum keeps ascending rank order.
+    for (int t0 = 0; t0 < T; t0 += 8)
 #pragma unroll
       for (int i = 0; i < KV; ++i) {
         const int v = tid + kNormThreads * i;
         if (v < hv) {
-          float f[8];
-          bf16x8_to_f32(ld16(Y + t * mh + row + v * 8), f);
+          u32x4 g[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sacc[i][e] += f[e];
+          for (int k = 0; k < 8; ++k)
+            if (t0 + k < T) g[k] = ld16(Y + (t0 + k) * mh + row + v * 8);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (t0 + k < T) {
+              float f[8];
+              bf16x8_to_f32(g[k], f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sacc[i][e] = t0 + k == 0 ? f[e] : sacc[i][e] + f[e];
+            }
         }
       }
   }

@@ -55,6 +55,8 @@ CASES = [
     (2, 5, 8192, "random", 0.5, 1e-5),    # the largest H: ranks in groups, Y read twice
     (3, 7, 776, "random", 0.75, 1e-6),    # odd rank count, H off every vector block
     (13, 6, 1024, "random", 0.5, 1e-5),   # more ranks than one group
+    (20, 5, 520, "strided", 0.5, 1e-5),   # runtime rank count: sums in groups of 8 + 8 + 4
+    (8, 6, 8192, "random", 0.5, 1e-5),    # eight ranks at the largest H: the runtime-T path
     (1, 3, 8, "random", 1.0, 0.5),        # one rank: the reduce is the identity
     (8, 20, 4096, "random", 0.0, 1e-5),   # nothing synced
     (8, 20, 4096, "random", 1.0, 1e-5),   # everything synced
