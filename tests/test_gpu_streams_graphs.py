@@ -2,10 +2,10 @@
 nothing, so its calls run on any stream and can be captured into a HIP graph
 (the decode kernel's arrival counters return to zero after every call).
 Checked here: a side stream gives the default stream's bits; a captured
-sequence (decode-shaped forward, split forward and its reduce pass, fused
-tiled forward, backward) replayed several times, with eager calls and
-synchronisation in between, reproduces the eager results bit for bit every
-time."""
+sequence (decode-shaped forward, whole and in contraction slices, split
+forward and its reduce pass, fused tiled forward, backward) replayed several
+times, with eager calls and synchronisation in between, reproduces the eager
+results bit for bit every time."""
 import numpy as np
 import pytest
 import torch
@@ -63,25 +63,34 @@ def test_graph_replays_match_eager(ops):
     Xf_, Wf_ = synth.make_fwd_inputs(T, Mf, Krf, H, seed=54)
     Xf, Wf = G.to_dev_bf16(Xf_), G.to_dev_bf16(Wf_)
     assert ops.fwd_workspace_bytes(T, Mf, Krf, H) == 0 and ops.fwd_workspace_bytes(T, Mt, Kr, H) > 2048
+    # a decode call with two ranks: each contraction in four slices
+    Ts, Krs = 2, 2056
+    Xs_, Ws_ = synth.make_fwd_inputs(Ts, Md, Krs, H, seed=55)
+    Xs, Ws = G.to_dev_bf16(Xs_), G.to_dev_bf16(Ws_)
+    assert ops.fwd_workspace_bytes(Ts, Md, Krs, H) == 2048 + 4 * Ts * Md * H * 4
     # every buffer exists before capture: nothing is allocated inside the graph
     o_dec = torch.empty((T, Md, H), dtype=torch.bfloat16, device=dev)
     o_t = torch.empty((T, Mt, H), dtype=torch.bfloat16, device=dev)
     o_f = torch.empty((T, Mf, H), dtype=torch.bfloat16, device=dev)
+    o_s = torch.empty((Ts, Md, H), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((T, Mt, Kr), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((T, Kr, H), dtype=torch.bfloat16, device=dev)
     ws_dec = torch.zeros(ops.fwd_workspace_bytes(T, Md, Kr, H), dtype=torch.uint8, device=dev)
     ws_t = torch.zeros(ops.fwd_workspace_bytes(T, Mt, Kr, H), dtype=torch.uint8, device=dev)
+    ws_s = torch.zeros(ops.fwd_workspace_bytes(Ts, Md, Krs, H), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(ops.bwd_workspace_bytes(T, Mt, Kr, H), dtype=torch.uint8, device=dev)
 
     def seq():
         ops.rowpar_pcr_fwd(Xdec, W, mask, out=o_dec, workspace=ws_dec)
         ops.rowpar_pcr_fwd(Xt, W, mask, out=o_t, workspace=ws_t)  # split forward + reduce pass
         ops.rowpar_pcr_fwd(Xf, Wf, mask, out=o_f)  # fused tiles, no workspace
+        ops.rowpar_pcr_fwd(Xs, Ws, mask, out=o_s, workspace=ws_s)  # decode in contraction slices
         ops.pcr_bwd(dZ, Xt, W, mask, dX=dX, dW=dW, workspace=ws_bwd)
 
     seq()
     torch.cuda.synchronize()
-    want = [t.clone() for t in (o_dec, o_t, o_f, dX, dW)]
+    outs = (o_dec, o_t, o_f, o_s, dX, dW)
+    want = [t.clone() for t in outs]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -96,11 +105,11 @@ def test_graph_replays_match_eager(ops):
 
     scratch = torch.empty_like(o_t)
     for rep in range(4):
-        for t in (o_dec, o_t, o_f, dX, dW):
+        for t in outs:
             t.fill_(0)
         g.replay()
         torch.cuda.synchronize()
-        for name, got, ref in zip(("decode out", "split out", "fused out", "dX", "dW"), (o_dec, o_t, o_f, dX, dW), want):
+        for name, got, ref in zip(("decode out", "split out", "fused out", "sliced decode out", "dX", "dW"), outs, want):
             assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), (rep, name)
         # eager work between replays, on other buffers
         ops.rowpar_pcr_fwd(Xt, W, mask, out=scratch)
@@ -108,6 +117,7 @@ def test_graph_replays_match_eager(ops):
     # the decode workspace's arrival counters are back at zero after the replays
     H_blocks = (H + 127) // 128
     assert int(ws_dec[: 4 * H_blocks].view(torch.int32).abs().sum().item()) == 0
+    assert int(ws_s[:2048].count_nonzero()) == 0
 
 
 def test_graph_replays_split_dw_backward(ops):
