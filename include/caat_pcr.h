@@ -124,7 +124,8 @@ size_t caat_rowpar_pcr_fwd_workspace_bytes(int T, int M, int Kr, int H);
  * even whole contractions do not fit, runs the path the shape would take
  * without the split (chunked decode or fused tiles); either gives the same
  * value up to fp32 summation order.  A decode call whose partials exceed it
- * (e.g. T*H > 131056 channels over all ranks at M = 32) returns
+ * (e.g. T*H > 131056 channels over all ranks at M = 32, whole contractions;
+ * calls in contraction slices need at most 4 MiB and always fit) returns
  * CAAT_ERR_WORKSPACE before anything is enqueued.  The scratch of the device
  * current at the call is used (`stream` must belong to it); its arrival
  * counters are cleared by the call itself (a small fill kernel, no memset).
