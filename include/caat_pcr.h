@@ -89,7 +89,9 @@ const char* caat_status_string(int status);
  *     of the 256 CUs and their token blocks at least 3/4) writes fp32
  *     products Y[T,M,H] into the workspace, and a
  *     streaming pass reduces them into out (the synced sum is the
- *     ascending-rank fp32 sum of the per-rank products).  With at most 256
+ *     ascending-rank fp32 sum of the per-rank products; with whole
+ *     contractions and H a multiple of 64, 64-channel groups with no synced
+ *     channel go straight to out and skip the pass).  With at most 256
  *     tiles of 128 x 64 and at least 16 chunks of 64 in each rank's
  *     contraction, that contraction is cut in two slices whose fp32 products
  *     (twice the workspace) are added first;

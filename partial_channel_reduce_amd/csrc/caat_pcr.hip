@@ -199,20 +199,21 @@ static uint32_t reduce_groups(const dim3& grid, long long slice_bytes, int T) {
 
 // Partial channel-reduce of fp32 y[T,M,H] into bf16 o (the split forward's
 // second pass).
-// (ks contraction slices per rank: y[q][t] at y + (q * T + t) * M * H.)
+// (ks contraction slices per rank: y[q][t] at y + (q * T + t) * M * H;
+// skip_local: the first pass wrote the wholly local 64-channel groups.)
 int launch_reduce_f32_bf16(const float* y, const uint8_t* mask, uint16_t* o, int T, int M, int H, int ks,
-                           hipStream_t s) {
+                           int skip_local, hipStream_t s) {
   const long long mh = (long long)M * H, ss = (long long)T * mh;
   const uint32_t nvec = (uint32_t)(mh / 4);
   const dim3 grid((nvec + kReduceThreads - 1) / kReduceThreads);
   const uint32_t hv = (uint32_t)(H / 4);
   const uint32_t hf = reduce_groups(grid, mh * 4, T);
   switch (T) {
-    case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
-    case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
-    case 8: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
-    case 16: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
-    default: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss); break;
+    case 2: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<2>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss, skip_local); break;
+    case 4: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<4>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss, skip_local); break;
+    case 8: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<8>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss, skip_local); break;
+    case 16: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss, skip_local); break;
+    default: hipLaunchKernelGGL(pcr_reduce_f32_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, hf, ks, ss, skip_local); break;
   }
   return launched();
 }
@@ -436,17 +437,21 @@ int fwd_launch(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uint16
     const int ks = Y ? std::min(split, pl.ks) : 1;  // bf16 straight to out: whole contractions
     const int tm = (H + pl.bm - 1) / pl.bm, tn = (M + pl.bn - 1) / pl.bn;
     const dim3 grid((unsigned)((long long)T * ks * tm * tn));
+    // With whole contractions and H a multiple of 64, the 64-channel groups
+    // with no synced channel go straight to out in bf16 and the second pass
+    // skips them.
+    const uint8_t* lmask = Y && ks == 1 && H % 64 == 0 ? mask : nullptr;
     if (pl.bm == 256)
       hipLaunchKernelGGL((rowpar_pcr_split_kernel<256, 256, kBigTileWaves>), grid, dim3(kBigTileWaves * 64), 0, s, X,
-                         W, out, Y, T, M, Kr, H, tm, tn, ks);
+                         W, out, Y, T, M, Kr, H, tm, tn, ks, lmask);
     else if (pl.bn == 128)
       hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 128, kSplitNW>), grid, dim3(kSplitNW * 64), 0, s, X, W,
-                         out, Y, T, M, Kr, H, tm, tn, ks);
+                         out, Y, T, M, Kr, H, tm, tn, ks, lmask);
     else
       hipLaunchKernelGGL((rowpar_pcr_split_kernel<kSplitBM, 64, kSplitNW>), grid, dim3(kSplitNW * 64), 0, s, X, W,
-                         out, Y, T, M, Kr, H, tm, tn, ks);
+                         out, Y, T, M, Kr, H, tm, tn, ks, lmask);
     if (int st = launched()) return st;
-    return Y ? launch_reduce_f32_bf16(Y, mask, out, T, M, H, ks, s) : CAAT_OK;
+    return Y ? launch_reduce_f32_bf16(Y, mask, out, T, M, H, ks, lmask != nullptr, s) : CAAT_OK;
   }
   if (use_decode(M, H)) {
     // workspace: the per-block arrival counters, then the fp32 partials

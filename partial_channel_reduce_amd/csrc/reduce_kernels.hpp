@@ -120,12 +120,15 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
 // 0's value, elsewhere Y[t]; one thread per 4-channel vector, T 16-byte loads
 // and T 8-byte stores.  With ks > 1 the products come in ks contraction
 // slices, Y[q][t] at Y + q * sstride + t * mh, and rank t's value is their
-// fp32 sum in slice order.
+// fp32 sum in slice order.  skip_local (H a multiple of 64): 64-channel
+// groups with no synced channel were written to out by the first pass (Y
+// holds nothing there); the 16 consecutive threads that cover such a group
+// find that out together and leave.
 template <int TC>  // TC = T known at compile time (1..16), or 0 for a runtime T
 __global__ void __launch_bounds__(kReduceThreads)
 pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
                            int T_rt, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups, int ks,
-                           long long sstride) {
+                           long long sstride, int skip_local) {
   const int T = TC > 0 ? TC : T_rt;
   constexpr int NR = TC > 0 ? TC : 1;  // ranks kept in registers
   const uint32_t v = reduce_block(groups) * kReduceThreads + threadIdx.x;
@@ -133,6 +136,14 @@ pcr_reduce_f32_bf16_kernel(const float* __restrict__ Y, const uint8_t* __restric
   const int c = (int)(v % hvec) * 4;
   const long long base = (long long)v * 4;
   const uint32_t mk = *reinterpret_cast<const uint32_t*>(mask + c);
+  if (skip_local) {
+    // nvec and the 64-channel groups are multiples of 16 threads, so the 16
+    // lanes of a group are all here
+    uint32_t any = mk;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) any |= __shfl_xor(any, o, 16);
+    if (any == 0u) return;
+  }
   const bool s0 = (mk & 0xffu) != 0, s1 = (mk & 0xff00u) != 0;
   const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
   // Runtime T: a rank's product (its slices in slice order) is read twice,

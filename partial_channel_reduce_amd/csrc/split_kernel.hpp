@@ -15,7 +15,12 @@
 //     second kernel, pcr_reduce_f32_bf16_kernel, forms the partial
 //     channel-reduce of Y into out: on synced channels the fp32 sum over the
 //     ranks in ascending order, starting from rank 0's value, rounded once
-//     (the same value on every rank); elsewhere the rank's own value.
+//     (the same value on every rank); elsewhere the rank's own value.  With
+//     whole contractions (ks == 1) and H a multiple of 64, a 64-channel group
+//     with no synced channel needs no sum: it goes straight to out[t] in bf16
+//     (the same rounding of the same value), and the second pass skips it,
+//     so a contiguous sync set moves half the fp32 bytes (a scattered one
+//     leaves practically no such group).
 // Per-rank products are fp32 MFMA sums over that rank's contraction (CAAT-Net
 // paper, Introduction: only the channels of the sync set are reduced over the
 // tensor-parallel ranks).  The kernel boundary orders the two passes, so no
@@ -38,7 +43,8 @@ constexpr int kSplitNW = 4;
 template <int BM, int BN, int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
 rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
-                        float* __restrict__ Y, int T, int M, int Kr, int H, int tiles_m, int tiles_n, int ks) {
+                        float* __restrict__ Y, int T, int M, int Kr, int H, int tiles_m, int tiles_n, int ks,
+                        const uint8_t* __restrict__ local_mask) {
   using S = TileShape<BM, BN, NW>;
   using RS = RowStage<S::WM>;
   static_assert(NW * S::WM * S::WN <= S::LDS_ELEMS, "final staging must fit");
@@ -106,8 +112,49 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
     return;
   }
   // fp32 to Y[q][t]: accumulator registers 4r..4r+3 of block (i, j) are 4
-  // consecutive channels of one token.
+  // consecutive channels of one token, lanes l and l + 32 the two halves of
+  // the 8-channel chunk chw + 32 i + 8 r.  With local_mask (whole
+  // contractions, H a multiple of 64) a 64-channel group with no synced
+  // channel goes to out[t] in bf16 instead, staged through this wave's part
+  // of LDS and written as whole lines.  The group flags depend on the wave's
+  // channels only, so the choice is uniform across its lanes.
+  constexpr int NG = S::WM / 64;  // 64-channel groups per wave: 1 or 2
+  static_assert(NG == 1 || NG == 2, "wave channel extent");
   float* yt = Y + ((long long)q * T + t) * MH;
+  // Lane l reads mask word l % 8 (8 channels) of group (l / 8) % NG; a
+  // group is direct when no lane of it saw a synced channel.
+  bool loc64[NG];
+  bool stage = false;
+  {
+    const int gl = (lane >> 3) & (NG - 1), cl = chw + 64 * gl + 8 * (lane & 7);
+    bool syn = true;
+    if (local_mask != nullptr && chw + 64 * gl < H) {
+      syn = false;
+      if (cl < H) {
+        const u32x2 m8 = *reinterpret_cast<const u32x2*>(local_mask + cl);
+        syn = (m8[0] | m8[1]) != 0u;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      loc64[g] = !__any(syn && gl == g);
+      stage |= loc64[g];
+    }
+  }
+  if (stage) {
+    uint16_t* st = smem + wave * (S::WM * S::WN);
+#pragma unroll
+    for (int i = 0; i < S::WI; ++i)
+#pragma unroll
+      for (int j = 0; j < S::WJ; ++j) RS::put(st, acc[i][j], i, j * 32, lane);
+    lds_wave_sync();
+    uint16_t* ou = out + t * MH;
+    RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 w) {
+      const int tok = tkw + r, ch = chw + cc * 8;
+      const bool direct = NG == 1 || cc * 8 < 64 ? loc64[0] : loc64[NG - 1];
+      if (direct && tok < M && ch < H) st16_nt(ou + (long long)tok * H + ch, w);
+    });
+  }
 #pragma unroll
   for (int i = 0; i < S::WI; ++i)
 #pragma unroll
@@ -116,8 +163,9 @@ rowpar_pcr_split_kernel(const uint16_t* __restrict__ X, const uint16_t* __restri
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ch = chw + i * 32 + r * 8 + (lane >> 5) * 4;
+        const bool direct = loc64[(i * 32 + r * 8) / 64];
         const f32x4 v = {acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]};
-        if (tok < M && ch < H) *reinterpret_cast<f32x4*>(yt + (long long)tok * H + ch) = v;
+        if (!direct && tok < M && ch < H) *reinterpret_cast<f32x4*>(yt + (long long)tok * H + ch) = v;
       }
     }
 }

@@ -191,3 +191,41 @@ def test_noalloc_fewer_slices(ops):
     s = np.flatnonzero(mask)
     for got in (got_n, got_w):
         assert all(np.array_equal(got[0][:, s], got[t][:, s]) for t in range(1, T))
+
+
+# Whole contractions with H a multiple of 64: 64-channel groups with no synced
+# channel go from the product kernel straight to out in bf16 and the reduce
+# pass skips them.  (T, M, Kr, H): 128 x 64 tiles (one group per wave),
+# 128 x 128 tiles (512 workgroups) and 256 x 256 tiles (two groups per wave,
+# ragged tokens).  Masks: a prefix whose end falls inside a group, alternating
+# 64-channel groups, a sparse random set (some groups wholly local, some
+# not), nothing synced (every group goes straight to out) and everything.
+LOCAL_SHAPES = [(8, 300, 136, 1024), (8, 1000, 136, 1024), (8, 1800, 136, 768)]
+
+
+def _local_mask(H, kind, seed):
+    if kind == "prefix47":
+        return synth.make_mask(H, 0.47, "prefix", seed=seed)
+    if kind == "alt64":
+        m = np.zeros(H, dtype=np.uint8)
+        for g in range(0, H, 128):
+            m[g:g + 64] = 1
+        return m
+    if kind == "sparse":
+        return synth.make_mask(H, 0.02, "random", seed=seed)
+    return synth.make_mask(H, 0.0 if kind == "none" else 1.0, "prefix", seed=seed)
+
+
+@pytest.mark.parametrize("T,M,Kr,H", LOCAL_SHAPES)
+@pytest.mark.parametrize("kind", ["prefix47", "alt64", "sparse", "none", "all"])
+def test_split_local_groups_bitwise(ops, T, M, Kr, H, kind):
+    assert H % 64 == 0 and ops.fwd_workspace_bytes(T, M, Kr, H) == 2048 + T * M * H * 4  # whole contractions
+    _announce(f"split local groups T={T} M={M} Kr={Kr} H={H} {kind}")
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=M + H, lo=-1, hi=1, x_zero_frac=0.4)
+    mask = _local_mask(H, kind, seed=M)
+    ref = oracle.rowpar_pcr_fwd(X, W, mask)
+    assert np.abs(ref).max() <= 256
+    out = torch.full((T, M, H), 7.0, dtype=torch.bfloat16, device=G.dev())  # every element must be written
+    ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(out), ref)
