@@ -236,12 +236,14 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
   // are written whole; otherwise each lane takes one channel and writes it
   // where synced (every synced channel, those of wholly synced chunks too).
   if (!__any(m8 != 0u && m8 != 0xffu)) {
-    RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
-      if (m8 == 0xffu && r < rows) {
-        uint16_t* o = out + (long long)(tkw + r) * H + chw + cc * 8;
-        for (int u = 0; u < T - 1; ++u) st16_nt(o + u * MH, v);
-      }
-    });
+    // Rank by rank: the output slices are M*H*2 bytes apart (128 MiB at the
+    // Llama2-7B shape), so the T-1 copies of one row piece would fall on
+    // the same HBM channels back to back; one rank's rows at a time spread
+    // the stores over them (the LDS is read T-1 times).
+    for (int u = 0; u < T - 1; ++u)
+      RS::drain(st, S::WN, lane, [&](int r, int cc, u32x4 v) {
+        if (m8 == 0xffu && r < rows) st16_nt(out + u * MH + (long long)(tkw + r) * H + chw + cc * 8, v);
+      });
     return;
   }
 #pragma unroll
@@ -250,11 +252,12 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
     const int ch = chw + cw;
     if (ch < H && mask[ch] != 0) {
       const uint16_t* sp = st + (cw & 7);
-      uint16_t* o = out + (long long)tkw * H + ch;
-      for (int r = 0; r < rows; ++r) {
-        const uint16_t v = sp[RS::off(r, cw >> 3)];
-        for (int u = 0; u < T - 1; ++u) __builtin_nontemporal_store(v, o + u * MH);
-        o += H;
+      for (int u = 0; u < T - 1; ++u) {  // rank by rank, as above
+        uint16_t* o = out + u * MH + (long long)tkw * H + ch;
+        for (int r = 0; r < rows; ++r) {
+          __builtin_nontemporal_store(sp[RS::off(r, cw >> 3)], o);
+          o += H;
+        }
       }
     }
   }
