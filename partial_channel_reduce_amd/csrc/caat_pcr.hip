@@ -82,6 +82,9 @@ int launch_fwd_rb(const uint16_t* X, const uint16_t* W, const uint8_t* mask, uin
   if (T <= 4)
     hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 4>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm,
                        tn, mode);
+  else if (tm * tn > 2 * kCUs && tm * tn <= 3 * kCUs)  // one round at three per CU, not at two
+    hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 8, 3>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H,
+                       tm, tn, mode);
   else
     hipLaunchKernelGGL((rowpar_pcr_fwd_rb_kernel<BM, BN, NW, 8>), grid, block, 0, s, X, W, mask, out, T, M, Kr, H, tm,
                        tn, mode);

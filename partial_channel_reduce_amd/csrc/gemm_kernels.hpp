@@ -281,9 +281,12 @@ rowpar_pcr_fwd_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict
 // (With TB = 8 the compiler is held to two workgroups per CU: a few rarely
 // touched values then live in scratch, and the second workgroup hides the
 // first one's latency -- T = 8, M = 8192, H = 768, Kr = 96: 67 -> 47 us, the
-// same bits.)
-template <int BM, int BN, int NW, int TB>
-__global__ void __launch_bounds__(NW * 64, TB > 4 ? 2 : 1)
+// same bits.  MINB = 3 holds it to three, with more values in scratch: that
+// pays only where three per CU take every tile in one round and two would
+// not, 513 to 768 tiles -- M = 8192, H = 768, Kr = 256 / 384 / 768: 75 / 91
+// / 147 -> 63 / 75 / 113 us; with thousands of tiles it loses 5-8%.)
+template <int BM, int BN, int NW, int TB, int MINB = (TB > 4 ? 2 : 1)>
+__global__ void __launch_bounds__(NW * 64, MINB)
 rowpar_pcr_fwd_rb_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out, int T, int M, int Kr, int H,
                          int tiles_m, int tiles_n, int mode) {

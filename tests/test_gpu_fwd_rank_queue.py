@@ -76,3 +76,28 @@ def test_fwd_rank_queue_run_to_run(ops):
     b = ops.rowpar_pcr_fwd(*args)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# Eight-rank queue tiles held to three workgroups per CU, the form taken when
+# 513 to 768 tiles of 128 x 64 fit one round at three per CU but not at two:
+# 585 tiles with every tile in the queue (Kr = 96), 658 with the two-launch
+# split of the mask's channel groups (Kr = 384, six chunks) and 768 at the
+# window's edge.
+THREE_PER_CU = [(8, 4100, 96, 1032), (6, 6000, 384, 776), (8, 8192, 256, 768)]
+
+
+@pytest.mark.parametrize("T,M,Kr,H", THREE_PER_CU)
+@pytest.mark.parametrize("kind,p", [("random", 0.5), ("prefix", 0.5), ("strided", 0.5), ("random", 0.1)])
+def test_fwd_rank_queue_three_per_cu_bitwise(ops, T, M, Kr, H, kind, p):
+    tiles = -(-H // 128) * -(-M // 64)
+    assert 512 < tiles <= 768
+    _announce(f"fwd rank queue 3/CU T={T} M={M} Kr={Kr} H={H} {kind} p={p}")
+    zf = 0.4 if T * Kr <= 1200 else 0.97
+    X, W = synth.make_integer_fwd_inputs(T, M, Kr, H, seed=T * 100 + Kr + 1, lo=-1, hi=1, x_zero_frac=zf)
+    mask = synth.make_mask(H, p, kind, seed=T + Kr + 1)
+    ref = oracle.rowpar_pcr_fwd(X, W, mask)
+    assert np.abs(ref).max() <= 256
+    out = torch.full((T, M, H), 7.0, dtype=torch.bfloat16, device=G.dev())
+    ops.rowpar_pcr_fwd(G.to_dev_bf16(X), G.to_dev_bf16(W), G.to_dev_u8(mask), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.from_dev_bf16(out), ref)
