@@ -114,6 +114,55 @@ pcr_reduce_f32_kernel(const float* Y, const uint8_t* __restrict__ mask, float* o
   }
 }
 
+// ---- fp32, T = 8, out of place: stores regrouped by rank --------------------
+// The eight rank slices of Y and out lie M*H*4 bytes apart (256 MiB at
+// M = 16384, H = 4096), so a thread's eight stores at one offset fall on the
+// same HBM channels.  Here the 512 threads of a workgroup leave their eight
+// output vectors in LDS and then wave t writes rank t's 8 KiB run of the
+// block: the same values and loads as pcr_reduce_f32_kernel<8>, the stores
+// in another order.
+constexpr int kReduceRunThreads = 512;
+
+__global__ void __launch_bounds__(kReduceRunThreads)
+pcr_reduce_f32_runs8_kernel(const float* __restrict__ Y, const uint8_t* __restrict__ mask, float* __restrict__ out,
+                            uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups) {
+  constexpr int TC = 8, NT = kReduceRunThreads;
+  static_assert(NT / 64 == TC, "one wave per rank");
+  __shared__ __attribute__((aligned(16))) f32x4 st[TC][NT];
+  const uint32_t blk0 = reduce_block(groups) * NT;
+  const uint32_t v = blk0 + threadIdx.x;
+  if (v < nvec) {
+    const int c = (int)(v % hvec) * 4;
+    const long long base = (long long)v * 4;
+    const uint32_t mk = *reinterpret_cast<const uint32_t*>(mask + c);
+    const bool s0 = (mk & 0xffu) != 0, s1 = (mk & 0xff00u) != 0;
+    const bool s2 = (mk & 0xff0000u) != 0, s3 = (mk & 0xff000000u) != 0;
+    f32x4 y[TC];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) y[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + t * mh + base));
+    f32x4 s = y[0];
+#pragma unroll
+    for (int t = 1; t < TC; ++t) s += y[t];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      f32x4 w;
+      w.x = s0 ? s.x : y[t].x;
+      w.y = s1 ? s.y : y[t].y;
+      w.z = s2 ? s.z : y[t].z;
+      w.w = s3 ? s.w : y[t].w;
+      st[t][threadIdx.x] = w;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const int j = k * 64 + lane;
+    if (blk0 + j < nvec)
+      __builtin_nontemporal_store(st[t][j], reinterpret_cast<f32x4*>(out + t * mh + (long long)(blk0 + j) * 4));
+  }
+}
+
 // ---- fp32 in, bf16 out: the second pass of the split forward ----------------
 // out[t] = bf16 of the partial channel-reduce of the fp32 per-rank products
 // Y[T,M,H]: on synced channels the ascending-rank fp32 sum starting from rank
@@ -338,6 +387,60 @@ pcr_reduce_bf16_kernel(const uint16_t* Y, const uint8_t* __restrict__ mask, uint
       for (int k = 0; k < 8; ++k)
         if (t0 + k < ranks_out) put(t0 + k, g[k]);
     }
+  }
+}
+
+// ---- bf16, T = 8, out of place: stores regrouped by rank --------------------
+// As pcr_reduce_f32_runs8_kernel for the bf16 reduce (the backward's G with
+// tile classes: a vector writes no rank, rank 0 only, or all eight).
+__global__ void __launch_bounds__(kReduceRunThreads)
+pcr_reduce_bf16_runs8_kernel(const uint16_t* __restrict__ Y, const uint8_t* __restrict__ mask,
+                             uint16_t* __restrict__ out, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups,
+                             const unsigned long long* __restrict__ tbits) {
+  constexpr int TC = 8, NT = kReduceRunThreads;
+  __shared__ __attribute__((aligned(16))) u32x4 st[TC][NT];
+  __shared__ uint8_t nout[NT];
+  const uint32_t blk0 = reduce_block(groups) * NT;
+  const uint32_t v = blk0 + threadIdx.x;
+  int ranks_out = 0;
+  if (v < nvec) {
+    const int c = (int)(v % hvec) * 8;
+    const long long base = (long long)v * 8;
+    ranks_out = TC;
+    if (tbits != nullptr) {
+      const int tile = c / kClassCols;
+      if ((tbits[1] >> tile) & 1ull) ranks_out = 0;
+      else if ((tbits[0] >> tile) & 1ull) ranks_out = 1;
+    }
+    if (ranks_out > 0) {
+      const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
+      const u32x4 sel = expand_mask8(mk[0], mk[1]);
+      u32x4 y[TC];
+#pragma unroll
+      for (int t = 0; t < TC; ++t) y[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Y + t * mh + base));
+      float s[8];
+      bf16x8_to_f32(y[0], s);
+#pragma unroll
+      for (int t = 1; t < TC; ++t) {
+        float f[8];
+        bf16x8_to_f32(y[t], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += f[e];
+      }
+      u32x4 sv;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
+#pragma unroll
+      for (int t = 0; t < TC; ++t) st[t][threadIdx.x] = (sv & sel) | (y[t] & ~sel);
+    }
+  }
+  nout[threadIdx.x] = (uint8_t)ranks_out;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const int j = k * 64 + lane;
+    if (blk0 + j < nvec && t < nout[j]) st16_nt(out + t * mh + (long long)(blk0 + j) * 8, st[t][j]);
   }
 }
 
