@@ -92,6 +92,8 @@ KERNEL_SOURCES = {
     "pcr_bwd_dx_kernel": _GEMM_SOURCES,
     "pcr_bwd_dw_kernel": _GEMM_SOURCES,
     "pcr_reduce_bf16_kernel": ("common.hpp", "reduce_kernels.hpp"),
+    "pcr_reduce_bf16_runs8_kernel": ("common.hpp", "reduce_kernels.hpp"),
+    "pcr_reduce_f32_runs8_kernel": ("common.hpp", "reduce_kernels.hpp"),
 }
 
 
