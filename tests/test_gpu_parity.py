@@ -52,6 +52,8 @@ RED_CASES = [
     (8, 1, 4096, "random", 0.5),
     (8, 32, 4096, "random", 1.0),
     (8, 16, 768, "random", 0.0),
+    (8, 7, 776, "strided", 0.5),    # T = 8 out of place: a partial last block of 512 vectors
+    (8, 3, 264, "prefix", 0.5),     # one partial block
     (13, 9, 200, "random", 0.5),
     (20, 17, 520, "strided", 0.5),  # runtime rank count: groups of 8 + 8 + 4
     (16, 33, 264, "random", 0.5),
@@ -92,7 +94,7 @@ def test_reduce_f32_inplace_leaves_local_sentinels(ops):
     assert np.all(got[:, :, ~S] == np.float32(-1234.5))
 
 
-@pytest.mark.parametrize("T,M,H,kind,p", RED_CASES[:6] + RED_CASES[-3:])
+@pytest.mark.parametrize("T,M,H,kind,p", RED_CASES[:6] + RED_CASES[8:10] + RED_CASES[-3:])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_reduce_bf16(ops, T, M, H, kind, p, inplace):
     _announce(f"reduce bf16 T={T} M={M} H={H} {kind} p={p} inplace={inplace}")
