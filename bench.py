@@ -94,6 +94,7 @@ KERNEL_SOURCES = {
     "pcr_reduce_bf16_kernel": ("common.hpp", "reduce_kernels.hpp"),
     "pcr_reduce_bf16_runs8_kernel": ("common.hpp", "reduce_kernels.hpp"),
     "pcr_reduce_f32_runs8_kernel": ("common.hpp", "reduce_kernels.hpp"),
+    "pcr_reduce_bf16_runs16_kernel": ("common.hpp", "reduce_kernels.hpp"),
 }
 
 

@@ -245,7 +245,16 @@ int launch_reduce_bf16(const uint16_t* y, const uint8_t* mask, uint16_t* o, int 
                            reduce_groups(g2, mh * 2, T), tbits);
       }
       break;
-    case 16: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
+    case 16:
+      if (ip) {
+        hipLaunchKernelGGL(pcr_reduce_bf16_kernel<16>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip,
+                           hf, tbits);
+      } else {  // stores regrouped by rank ([16,16384,4096]: 780 -> 737 us)
+        const dim3 g2((nvec + kReduceRunThreads - 1) / kReduceRunThreads);
+        hipLaunchKernelGGL(pcr_reduce_bf16_runs16_kernel, g2, dim3(kReduceRunThreads), 0, s, y, mask, o, nvec, hv, mh,
+                           reduce_groups(g2, mh * 2, T), tbits);
+      }
+      break;
     default: hipLaunchKernelGGL(pcr_reduce_bf16_kernel<0>, grid, dim3(kReduceThreads), 0, s, y, mask, o, T, nvec, hv, mh, ip, hf, tbits); break;
   }
   return launched();

@@ -444,6 +444,64 @@ pcr_reduce_bf16_runs8_kernel(const uint16_t* __restrict__ Y, const uint8_t* __re
   }
 }
 
+// ---- bf16, T = 16, out of place: stores regrouped by rank -------------------
+// As pcr_reduce_bf16_runs8_kernel with sixteen ranks: each wave writes two
+// ranks' 8 KiB runs of the block (128 KiB of LDS).
+__global__ void __launch_bounds__(kReduceRunThreads)
+pcr_reduce_bf16_runs16_kernel(const uint16_t* __restrict__ Y, const uint8_t* __restrict__ mask,
+                              uint16_t* __restrict__ out, uint32_t nvec, uint32_t hvec, long long mh, uint32_t groups,
+                              const unsigned long long* __restrict__ tbits) {
+  constexpr int TC = 16, NT = kReduceRunThreads;
+  __shared__ __attribute__((aligned(16))) u32x4 st[TC][NT];
+  __shared__ uint8_t nout[NT];
+  const uint32_t blk0 = reduce_block(groups) * NT;
+  const uint32_t v = blk0 + threadIdx.x;
+  int ranks_out = 0;
+  if (v < nvec) {
+    const int c = (int)(v % hvec) * 8;
+    const long long base = (long long)v * 8;
+    ranks_out = TC;
+    if (tbits != nullptr) {
+      const int tile = c / kClassCols;
+      if ((tbits[1] >> tile) & 1ull) ranks_out = 0;
+      else if ((tbits[0] >> tile) & 1ull) ranks_out = 1;
+    }
+    if (ranks_out > 0) {
+      const u32x2 mk = *reinterpret_cast<const u32x2*>(mask + c);
+      const u32x4 sel = expand_mask8(mk[0], mk[1]);
+      u32x4 y[TC];
+#pragma unroll
+      for (int t = 0; t < TC; ++t) y[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Y + t * mh + base));
+      float s[8];
+      bf16x8_to_f32(y[0], s);
+#pragma unroll
+      for (int t = 1; t < TC; ++t) {
+        float f[8];
+        bf16x8_to_f32(y[t], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += f[e];
+      }
+      u32x4 sv;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) sv[d] = pack_bf16x2(s[2 * d], s[2 * d + 1]);
+#pragma unroll
+      for (int t = 0; t < TC; ++t) st[t][threadIdx.x] = (sv & sel) | (y[t] & ~sel);
+    }
+  }
+  nout[threadIdx.x] = (uint8_t)ranks_out;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int t = 2 * wave + rr;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) {
+      const int j = k * 64 + lane;
+      if (blk0 + j < nvec && t < nout[j]) st16_nt(out + t * mh + (long long)(blk0 + j) * 8, st[t][j]);
+    }
+  }
+}
+
 // Small fill kernel (used instead of a runtime memset so the call sequence can
 // be captured in a graph).
 __global__ void fill_u32_kernel(uint32_t* p, long long n, uint32_t v) {
