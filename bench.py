@@ -136,7 +136,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(
             "bench.py measures one GPU: the T tensor-parallel ranks are resident shards on a single "
-            "MI355X; runs on more than one GPU are not part of this build.",
+            "MI355X; a run across several GPUs is not measured here.",
             file=sys.stderr,
         )
         sys.exit(2)
