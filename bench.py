@@ -81,7 +81,69 @@ def parse():
     ap.add_argument("--rocprof-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-kernel HBM bytes from two rocprofv3 --pmc csv runs (FETCH_SIZE, WRITE_SIZE), "
                          "calibrated against the copy leg's kernel, and exit")
+    ap.add_argument("--rocprof-channel-yaml", metavar="PATH",
+                    help="write the per-L2-channel counter definitions (for rocprofv3 -E) to PATH, and exit")
+    ap.add_argument("--rocprof-channels", nargs="+", metavar="DIR",
+                    help="per-L2-channel totals and spread of the fp32 reduce (its largest launch) from rocprofv3 "
+                         "--pmc csv runs made with the --rocprof-channel-yaml counters, and exit")
     return ap.parse_args()
+
+
+# Per-L2-channel counters: each TCC counter below has one value per channel
+# (16 per XCD) and per XCD; a derived counter per channel sums one channel
+# over the eight XCDs.  Two passes (at most four TCC base counters each): the
+# DRAM credit stalls with the busy cycles, and the requests.
+CHANNEL_PASSES = ((("RST", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL"), ("WST", "TCC_EA0_WRREQ_DRAM_CREDIT_STALL"),
+                   ("BUSY", "TCC_BUSY")),
+                  (("RD", "TCC_EA0_RDREQ"), ("WR", "TCC_EA0_WRREQ")))
+CHANNEL_COUNTERS = tuple(c for p in CHANNEL_PASSES for c in p)
+N_L2_CHANNELS = 16
+
+
+def channel_counter_yaml() -> str:
+    out = ["rocprofiler-sdk:", "  counters-schema-version: 1", "  counters:"]
+    for tag, base in CHANNEL_COUNTERS:
+        for k in range(N_L2_CHANNELS):
+            out += [f"  - name: {tag}_CH{k}", f"    description: {base} of L2 channel {k}, summed over the XCDs",
+                    "    properties: []", "    definitions:", "    - architectures:", "      - gfx950",
+                    f"      expression: reduce(select({base},[DIMENSION_INSTANCE=[{k}]]),sum)"]
+    return "\n".join(out) + "\n"
+
+
+def channel_counter_names() -> str:
+    """One line per pass: the derived counters to hand to --pmc."""
+    return "\n".join(" ".join(f"{tag}_CH{k}" for tag, _ in p for k in range(N_L2_CHANNELS)) for p in CHANNEL_PASSES)
+
+
+def rocprof_channels_summary(dirs) -> str:
+    """Per-channel medians over the fp32 reduce's largest launches, one block per run."""
+    import statistics as st
+    out = []
+    for d in dirs:
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv"))
+                if "pcr_reduce_f32" in r["Kernel_Name"]]
+        if not rows:
+            out.append(f"{d}: no fp32 reduce launch")
+            continue
+        g = max(int(r["Grid_Size"]) for r in rows)
+        per, dur = {}, {}
+        for r in rows:
+            if int(r["Grid_Size"]) != g:
+                continue
+            per.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+            dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        out.append(f"{d}: {len(dur)} launches of {g} threads, profiled duration median {st.median(dur.values()):.0f} us")
+        out.append("| counter | total (M) | max / mean | min / mean | cv | per channel (M) |")
+        out.append("|---|---|---|---|---|---|")
+        for tag, base in CHANNEL_COUNTERS:
+            if f"{tag}_CH0" not in per:
+                continue
+            v = [st.median(per[f"{tag}_CH{k}"].values()) for k in range(N_L2_CHANNELS)]
+            m = st.mean(v)
+            out.append(f"| {base} | {sum(v) / 1e6:.2f} | {max(v) / m:.3f} | {min(v) / m:.3f} | "
+                       f"{st.pstdev(v) / m:.3f} | " + " ".join(f"{x / 1e6:.2f}" for x in v) + " |")
+        out.append("")
+    return "\n".join(out)
 
 
 # The sources each counted kernel is compiled from (its device code; the host
@@ -131,6 +193,14 @@ def main():
         return
     if args.rocprof_traffic:
         print(rocprof_traffic_summary(*args.rocprof_traffic))
+        return
+    if args.rocprof_channel_yaml:
+        with open(args.rocprof_channel_yaml, "w") as f:
+            f.write(channel_counter_yaml())
+        print(channel_counter_names())
+        return
+    if args.rocprof_channels:
+        print(rocprof_channels_summary(args.rocprof_channels))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
